@@ -1,0 +1,346 @@
+"""Pins for the CPU oracle: checks against what the definition and the
+mathematics fix, independent of the oracle's own code.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError on a
+mismatch.  ``test_oracle_pins.py`` runs them on the oracle as built;
+``test_oracle_mutants.py`` runs them on copies of the oracle with a planted
+mistake and requires every mutant to fail at least one pin.
+
+What pins what:
+* binary16 encoding   -- numpy's float16 cast (IEEE round to nearest even)
+                         and the exhaustive round trip of every binary16;
+* block quantiser     -- hand-derived cases (tests/golden), an exact
+                         rational re-derivation of each binary32 step
+                         (oracle/exact.py), and invariants of the format;
+* block integer dots  -- numpy int64 products;
+* the product         -- hand-derived cases, an exact rational
+                         dequantise-then-multiply brute force, and the
+                         unit-scale case where C is an exact integer;
+* GGUF block bytes and the packed layout -- hand-picked byte positions.
+"""
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+
+from oracle import exact
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# --------------------------------------------------------------------------
+# golden file parsing
+# --------------------------------------------------------------------------
+
+def _num(tok):
+    t = tok.lstrip("-")
+    v = float.fromhex(t) if t.startswith("0x") else float(t)
+    return -v if tok.startswith("-") else v
+
+
+def _pad32(vals):
+    vals = list(vals)
+    assert len(vals) <= 32
+    return vals + [0] * (32 - len(vals))
+
+
+def load_block_cases():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "q8_0_block_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, rest = line.partition(" ")
+            toks = [t for t in rest.split() if t != "..."]
+            if key == "case":
+                cur = {"name": rest.strip()}
+                cases.append(cur)
+            elif key == "x":
+                xs = _pad32([_num(t) for t in toks])
+                x32 = np.array(xs, dtype=np.float32)
+                assert np.array_equal(x32.astype(np.float64), np.array(xs)), \
+                    "golden x not exact in binary32: %s" % cur["name"]
+                cur["x"] = x32
+            elif key == "q":
+                cur["q"] = np.array(_pad32(int(t) for t in toks), dtype=np.int8)
+            elif key == "d":
+                cur["d"] = int(rest.strip(), 16)
+    return cases
+
+
+def _rle(toks):
+    out = []
+    for t in toks:
+        v, _, c = t.partition("*")
+        out += [int(v)] * (int(c) if c else 1)
+    return out
+
+
+def load_gemm_cases():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "q8_0_gemm_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, rest = line.partition(" ")
+            if key == "case":
+                cur = {"name": rest.strip(), "C": {}, "absdot": {}}
+                cases.append(cur)
+            elif key == "shape":
+                M, N, K = map(int, rest.split())
+                cur.update(M=M, N=N, K=K,
+                           qa=np.zeros((M, K), np.int8), qw=np.zeros((N, K), np.int8),
+                           da=np.zeros((M, K // 32), np.uint16),
+                           dw=np.zeros((N, K // 32), np.uint16))
+            elif key in ("qa", "qw"):
+                r, _, vals = rest.partition(":")
+                cur[key][int(r)] = np.array(_rle(vals.split()), dtype=np.int8)
+            elif key in ("da", "dw"):
+                r, _, vals = rest.partition(":")
+                cur[key][int(r)] = [int(v, 16) for v in vals.split()]
+            elif key in ("C", "absdot"):
+                m, n, v = rest.split()
+                cur[key][(int(m), int(n))] = Fraction(v)
+    return cases
+
+
+# --------------------------------------------------------------------------
+# binary16
+# --------------------------------------------------------------------------
+
+def pin_f16_roundtrip_all(orc):
+    """Every finite binary16 value converts back to its own bits."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7C00) != 0x7C00
+    bits = bits[finite]
+    vals = bits.view(np.float16).astype(np.float32)
+    got = orc.f32_to_f16_bits(vals)
+    # -0 and +0 keep their sign
+    assert np.array_equal(got, bits), "binary16 round trip differs"
+
+
+def pin_f16_vs_numpy(orc):
+    """Ties, near-ties, overflow edge and random values against numpy's
+    float16 cast (IEEE 754 round to nearest even)."""
+    h = np.arange(0, 0x7BFF, dtype=np.uint16)            # positive finite, not max
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    mid = ((lo + hi) / 2).astype(np.float32)             # exact: <= 12 bits
+    xs = [mid,
+          np.nextafter(mid, np.float32(np.inf)),
+          np.nextafter(mid, np.float32(0)),
+          np.array([65504, 65519.996, 65520, 1e5, 2.0 ** -25, 2.0 ** -26,
+                    3 * 2.0 ** -26, 2.0 ** -24, 1e-30, 0.0], dtype=np.float32)]
+    r = np.random.default_rng(7)
+    xs.append((r.standard_normal(200000) * np.exp2(r.uniform(-30, 17, 200000))).astype(np.float32))
+    x = np.concatenate(xs).astype(np.float32)
+    x = np.concatenate([x, -x])
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    got = orc.f32_to_f16_bits(x)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, "binary16 differs from numpy at %r" % (x[bad[:5]],)
+
+
+# --------------------------------------------------------------------------
+# block quantiser
+# --------------------------------------------------------------------------
+
+def pin_quant_golden(orc):
+    for c in load_block_cases():
+        q, d, st = orc.quantize_block(c["x"])
+        assert st == 0, c["name"]
+        assert np.array_equal(q, c["q"]), "%s: q %s" % (c["name"], q)
+        assert d == c["d"], "%s: d %#06x want %#06x" % (c["name"], d, c["d"])
+
+
+def _random_blocks(n, seed):
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = i % 5
+        x = r.standard_normal(32)
+        if kind == 1:
+            x *= 10.0 ** r.uniform(-6, 6)
+        elif kind == 2:                       # integer-ish values -> many ties
+            x = np.round(r.uniform(-127, 127, 32) * 2) / 2
+        elif kind == 3:                       # fp16-subnormal scales
+            x *= 2.0 ** r.uniform(-24, -14)
+        elif kind == 4:                       # one outlier
+            x[r.integers(32)] *= 50
+        out.append(x.astype(np.float32))
+    return out
+
+
+def pin_quant_exact_random(orc, n=300):
+    """Each binary32 step re-derived with exact rationals (oracle/exact.py)."""
+    for x in _random_blocks(n, 11):
+        q, d, st = orc.quantize_block(x)
+        qe, de = exact.quantize_block_exact([float(v) for v in x])
+        assert st == 0
+        assert list(q.astype(int)) == qe, "q differs from exact re-derivation for %r" % (x,)
+        assert d == de, "d %#06x != exact %#06x" % (d, de)
+
+
+def pin_quant_invariants(orc, n=400):
+    """|q| <= 127; the amax element maps to +-127; q(-x) = -q(x); scaling by
+    2^e leaves q unchanged and scales d32; |x - d32 q| <= d32/2 (+ rounding)."""
+    for x in _random_blocks(n, 12):
+        q, d, _ = orc.quantize_block(x)
+        amax = np.max(np.abs(x))
+        d32 = np.float32(amax) / np.float32(127)
+        assert np.all(np.abs(q.astype(int)) <= 127)
+        if d32 >= np.finfo(np.float32).tiny:
+            i = int(np.argmax(np.abs(x)))
+            assert abs(int(q[i])) == 127
+            err = np.abs(x.astype(np.float64) - float(d32) * q.astype(np.float64))
+            assert np.all(err <= float(d32) * (0.5 + 2.0 ** -20)), "reconstruction bound"
+        qn, dn, _ = orc.quantize_block(-x)
+        assert np.array_equal(qn, -q) and dn == d
+        for e in (-3, 5):
+            xs = (x * np.float32(2.0 ** e)).astype(np.float32)
+            qs, ds, _ = orc.quantize_block(xs)
+            if np.float32(amax) * np.float32(2.0 ** min(e, 0)) > 1e-30:
+                assert np.array_equal(qs, q), "q changed under power-of-two scaling"
+
+
+def pin_quant_rows(orc):
+    """Rows: bfloat16 input equals its exact binary32 widening; ldx > K
+    ignores trailing columns; every block equals the single-block call."""
+    r = np.random.default_rng(3)
+    M, K, ldx = 5, 96, 128
+    x = (r.standard_normal((M, ldx)) * 3).astype(np.float32)
+    q, d = orc.quantize_rows(x, K=K, ldx=ldx)
+    for m in range(M):
+        for kb in range(K // 32):
+            qb, db, _ = orc.quantize_block(x[m, 32 * kb:32 * kb + 32])
+            assert np.array_equal(q[m, 32 * kb:32 * kb + 32], qb) and d[m, kb] == db
+    b = (x.view(np.uint32) >> 16).astype(np.uint16)       # some bfloat16 bits
+    wide = (b.astype(np.uint32) << 16).view(np.float32)
+    qb16, db16 = orc.quantize_rows(b, K=K, ldx=ldx)
+    qf, df = orc.quantize_rows(np.ascontiguousarray(wide), K=K, ldx=ldx)
+    assert np.array_equal(qb16, qf) and np.array_equal(db16, df)
+
+
+# --------------------------------------------------------------------------
+# the product
+# --------------------------------------------------------------------------
+
+def pin_gemm_golden(orc):
+    for c in load_gemm_cases():
+        C, A = orc.gemm(c["qa"], c["da"], c["qw"], c["dw"])
+        for (m, n), v in c["C"].items():
+            assert Fraction(C[m, n]) == v, "%s C[%d][%d] = %r" % (c["name"], m, n, C[m, n])
+        for (m, n), v in c["absdot"].items():
+            assert Fraction(A[m, n]) == v, "%s absdot[%d][%d]" % (c["name"], m, n)
+
+
+def _tiny_problem(seed, M, N, K):
+    r = np.random.default_rng(seed)
+    qa = r.integers(-127, 128, (M, K)).astype(np.int8)
+    qw = r.integers(-127, 128, (N, K)).astype(np.int8)
+    da = (np.abs(r.standard_normal((M, K // 32))) * 0.02 + 1e-4).astype(np.float16).view(np.uint16)
+    dw = (np.abs(r.standard_normal((N, K // 32))) * 4e-4 + 1e-6).astype(np.float16).view(np.uint16)
+    sa = r.choice([-1, 1], size=da.shape)
+    da = np.where(sa < 0, da | 0x8000, da).astype(np.uint16)
+    return qa, da, qw, dw
+
+
+def pin_gemm_exact(orc):
+    """Against exact rational dequantise-then-multiply, on tiny shapes."""
+    for seed, (M, N, K) in enumerate([(3, 4, 64), (2, 5, 96), (1, 3, 160)]):
+        qa, da, qw, dw = _tiny_problem(100 + seed, M, N, K)
+        C, A = orc.gemm(qa, da, qw, dw)
+        E = exact.gemm_exact(qa.tolist(), da.tolist(), qw.tolist(), dw.tolist())
+        for m in range(M):
+            for n in range(N):
+                err = abs(Fraction(C[m, n]) - E[m][n])
+                assert err <= Fraction(A[m, n]) * Fraction(1, 2 ** 48), (m, n, float(err))
+                assert A[m, n] >= abs(C[m, n])
+
+
+def pin_gemm_unit_scale(orc):
+    """With every scale 1.0 the product is the integer matrix product."""
+    r = np.random.default_rng(5)
+    M, N, K = 7, 9, 1024
+    qa = r.integers(-127, 128, (M, K)).astype(np.int8)
+    qw = r.integers(-127, 128, (N, K)).astype(np.int8)
+    ones_a = np.full((M, K // 32), 0x3C00, np.uint16)
+    ones_w = np.full((N, K // 32), 0x3C00, np.uint16)
+    C, _ = orc.gemm(qa, ones_a, qw, ones_w)
+    want = qa.astype(np.int64) @ qw.astype(np.int64).T
+    assert np.array_equal(C, want.astype(np.float64))
+
+
+def pin_block_dots(orc):
+    r = np.random.default_rng(6)
+    M, N, K = 3, 4, 128
+    qa = r.integers(-127, 128, (M, K)).astype(np.int8)
+    qw = r.integers(-127, 128, (N, K)).astype(np.int8)
+    P = orc.block_dots(qa, qw)
+    want = np.einsum("mbj,nbj->mnb", qa.reshape(M, K // 32, 32).astype(np.int64),
+                     qw.reshape(N, K // 32, 32).astype(np.int64))
+    assert np.array_equal(P, want)
+
+
+def pin_gemm_sampled(orc):
+    qa, da, qw, dw = _tiny_problem(9, 6, 10, 128)
+    C, A = orc.gemm(qa, da, qw, dw)
+    rows = np.array([0, 5, 3, 2, 5])
+    cols = np.array([9, 0, 4, 4, 7])
+    Cs, As = orc.gemm_sampled(qa, da, qw, dw, rows, cols)
+    assert np.array_equal(Cs, C[rows, cols]) and np.array_equal(As, A[rows, cols])
+
+
+# --------------------------------------------------------------------------
+# byte layouts
+# --------------------------------------------------------------------------
+
+def pin_block_bytes(orc):
+    """GGUF Q8_0 block = binary16 d (little-endian) then int8 q[32]."""
+    q = np.arange(-32, 32, dtype=np.int8).reshape(1, 64)
+    d = np.array([[0x3C01, 0xABCD]], dtype=np.uint16)
+    b = orc.blocks_from_qd(q, d)
+    assert b.shape == (1, 68)
+    assert list(b[0, :2]) == [0x01, 0x3C] and list(b[0, 34:36]) == [0xCD, 0xAB]
+    assert list(b[0, 2:34].view(np.int8)) == list(range(-32, 0))
+    assert list(b[0, 36:68].view(np.int8)) == list(range(0, 32))
+    q2, d2 = orc.qd_from_blocks(b, 1, 64)
+    assert np.array_equal(q2, q) and np.array_equal(d2, d)
+
+
+def pin_pack_layout(orc):
+    """Hand-picked byte positions of the packed layout (see include/q8.h):
+    quant byte ((g*KB + kb)*2 + h)*1024 + r*16 + t = q[64g+r][32kb+16h+t];
+    scale (g*KB + kb)*64 + r after the quant plane; rows >= N are zero."""
+    N, K = 70, 96                       # 2 row groups (second one ragged), 3 blocks
+    KB, NG = 3, 2
+    r = np.random.default_rng(8)
+    q = r.integers(-127, 128, (N, K)).astype(np.int8)
+    d = r.integers(1, 0x7BFF, (N, KB)).astype(np.uint16)
+    packed = orc.pack(orc.blocks_from_qd(q, d), N, K)
+    assert packed.size == NG * KB * (2048 + 128) == orc.packed_bytes(N, K)
+    qp = packed[:NG * KB * 2048].view(np.int8)
+    sp = packed[NG * KB * 2048:].view(np.uint16)
+    for (g, kb, h, rr, t) in [(0, 0, 0, 0, 0), (0, 1, 1, 2, 3), (1, 2, 0, 5, 15),
+                              (0, 2, 1, 63, 15), (1, 0, 1, 0, 7)]:
+        assert qp[((g * KB + kb) * 2 + h) * 1024 + rr * 16 + t] == q[64 * g + rr, 32 * kb + 16 * h + t]
+    for (g, kb, rr) in [(0, 0, 0), (0, 2, 17), (1, 1, 5)]:
+        assert sp[(g * KB + kb) * 64 + rr] == d[64 * g + rr, kb]
+    # rows 70..127 of group 1 are padding: zero quants and scales
+    for kb in range(KB):
+        for h in range(2):
+            base = ((1 * KB + kb) * 2 + h) * 1024
+            assert not np.any(qp[base + 6 * 16: base + 1024])
+        assert not np.any(sp[(1 * KB + kb) * 64 + 6:(1 * KB + kb) * 64 + 64])
+    # a permutation: the multiset of real bytes is preserved
+    assert sorted(qp[qp != 0].tolist()) == sorted(q[q != 0].tolist())
+
+
+ALL_PINS = [pin_f16_roundtrip_all, pin_f16_vs_numpy, pin_quant_golden, pin_quant_exact_random,
+            pin_quant_invariants, pin_quant_rows, pin_gemm_golden, pin_gemm_exact,
+            pin_gemm_unit_scale, pin_block_dots, pin_gemm_sampled, pin_block_bytes,
+            pin_pack_layout]

@@ -1,0 +1,61 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutant is a copy of oracle/q8ref.c with one plausible mistake (a dropped
+term, a wrong index or sign, a transposed operand, a wrong rounding rule),
+compiled with the oracle's own flags into a temporary library and run
+through every pin of tests/pins.py on the CPU.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+import pins
+
+MUTANTS = {
+    "scale_divisor_128": ("float d32 = amax / 127.0f;", "float d32 = amax / 128.0f;"),
+    "ties_toward_zero": ("(frac >= 0.5f) ? t + 1.0f : t", "(frac > 0.5f) ? t + 1.0f : t"),
+    "divide_instead_of_reciprocal": ("float v = x[j] * id;", "float v = x[j] / d32;"),
+    "f16_ties_away": ("if (rem > half || (rem == half && (q & 1u))) q += 1u;",
+                      "if (rem >= half) q += 1u;"),
+    "f16_subnormal_shift": ("shift_rne(sig, -(e + 1));", "shift_rne(sig, -e);"),
+    "zero_test_exact": ("if (d32 < FLT_MIN) {", "if (d32 == 0.0f) {"),
+    "bf16_shift": ("(uint32_t)b << 16;", "(uint32_t)b << 15;"),
+    "drop_last_block": ("acc += s * (double)p;", "acc += (kb + 1 < KB) ? s * (double)p : 0.0;"),
+    "weight_scale_index": ("q8ref_f16_to_f64(dw_row[kb])", "q8ref_f16_to_f64(dw_row[0])"),
+    "activation_times_itself": ("int32_t p = block_dot(qa_row + kb * QK, qw_row + kb * QK);",
+                                "int32_t p = block_dot(qa_row + kb * QK, qa_row + kb * QK);"),
+    "reversed_weight_index": ("s += (int32_t)a[j] * (int32_t)w[j];",
+                              "s += (int32_t)a[j] * (int32_t)w[QK - 1 - j];"),
+    "transposed_output": ("C[m * N + n] = c;", "C[n * M + m] = c;"),
+    "absdot_signed": ("mag += fabs(s) *", "mag += s *"),
+    "block_endianness": ("b[0] = (uint8_t)(h & 0xff);\n            b[1] = (uint8_t)(h >> 8);",
+                         "b[1] = (uint8_t)(h & 0xff);\n            b[0] = (uint8_t)(h >> 8);"),
+    "pack_row_stride": ("* 1024 + r * 16 + t] =", "* 1024 + t * 64 + r] ="),
+    "pack_half_order": ("b ? b[2 + 16 * h + t] : 0;", "b ? b[2 + 16 * (1 - h) + t] : 0;"),
+    "sampled_wrong_row": ("one_output(q_a + rows[i] * K, d_a + rows[i] * KB,",
+                          "one_output(q_a + cols[i] * K, d_a + rows[i] * KB,"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_fails_a_pin(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(obuild.SRC).read()
+    assert src.count(old) == 1, "mutation site not unique/not found: %s" % name
+    path_c = tmp_path / ("q8ref_%s.c" % name)
+    path_c.write_text(src.replace(old, new))
+    lib = str(tmp_path / ("libq8ref_%s.so" % name))
+    subprocess.run(["gcc", *obuild.CFLAGS, str(path_c), "-o", lib, "-lm"], check=True)
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+        except Exception as e:          # a crash or a shape error also counts
+            failed.append("%s (%s)" % (pin.__name__, type(e).__name__))
+    assert failed, "planted mistake %r passed every pin" % name
