@@ -1,0 +1,142 @@
+/*
+ * q8.h -- C ABI of libq8gemm: the Q8_0 weight x activation product on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Source of the operation.  news.hada.io topic 29953, "CUDA inference engine
+ * for running Qwen3.5/3.6 hybrid models on mining cards (CMP 100-210)":
+ * its list of paths that avoid the throttled units does the model's GEMMs
+ * with a self-written int8 DP4A kernel, and its benchmark and limitations
+ * lists name Q8_0 GGUF as the one supported weight format.  Q8_0 stores 32
+ * consecutive values along K as int8 q[32] plus one IEEE binary16 scale d
+ * (value = d*q).  Activations are quantised on the fly into the same block
+ * format, so each output is
+ *
+ *     C[m][n] = sum_kb  d_a[m][kb] * d_w[n][kb] * int32( sum_{j<32} q_a[m][32kb+j] * q_w[n][32kb+j] )
+ *
+ * i.e. C = A * W^T with A = tokens x K and W = output features x K.
+ *
+ * Conventions for every call:
+ *   - all data pointers are DEVICE pointers of the current HIP device;
+ *   - work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the null stream); calls return at once, never synchronise, never
+ *     allocate, and keep no state beyond a one-time per-device check;
+ *   - arguments are validated on the host before any HIP call; a failed
+ *     check returns its status and enqueues nothing;
+ *   - the caller owns every buffer; outputs are overwritten, never read;
+ *   - faults during execution surface at the caller's next synchronisation,
+ *     as for any HIP kernel.
+ *   - input/output buffers must not overlap.
+ *
+ * Domain: finite inputs whose block maxima stay below 65504*127 (larger
+ * scales overflow binary16).  NaN and infinity are outside the domain.
+ */
+#ifndef Q8_H
+#define Q8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q8_OK = 0,
+    Q8_ERR_NULL = 1,    /* a required pointer is NULL                        */
+    Q8_ERR_SHAPE = 2,   /* K <= 0 or K % 32 != 0, N <= 0, M < 0, ldx < K,
+                           ldc < N, or a size too large for the kernels      */
+    Q8_ERR_ALIGN = 3,   /* a pointer or a row pitch breaks the stated alignment */
+    Q8_ERR_DTYPE = 4,   /* unknown q8_dtype                                  */
+    Q8_ERR_SIZE = 5,    /* *packed_bytes smaller than the packed layout      */
+    Q8_ERR_DEVICE = 6,  /* the current device is not gfx950, or no device    */
+    Q8_ERR_LAUNCH = 7   /* the kernel launch was rejected by the runtime     */
+} q8_status;
+
+typedef enum {
+    Q8_F32 = 0,         /* IEEE binary32                                     */
+    Q8_BF16 = 1         /* bfloat16 (upper half of a binary32)               */
+} q8_dtype;
+
+/*
+ * q8_pack_weights -- repack Q8_0 weight rows into the layout q8_gemm reads.
+ *
+ * Operation: a byte permutation of the GGUF Q8_0 blocks (the format the
+ * source names, see above); no arithmetic.  Done once when weights load.
+ *
+ * w_blocks  [N][K/32] blocks of 34 bytes: binary16 d (little-endian), then
+ *           int8 q[32]; block (n, kb) at byte (n*(K/32) + kb)*34.  Any
+ *           alignment.
+ * N, K      output features and reduction length; N >= 1, K >= 32,
+ *           K % 32 == 0.
+ * w_packed  device buffer, 16-byte aligned, or NULL to query the size.
+ * packed_bytes  in: capacity of w_packed; out (when w_packed is NULL): the
+ *           required size, NG*KB*2176 with NG = ceil(N/64), KB = K/32
+ *           (= 1.0625*N*K bytes when N % 64 == 0).
+ *
+ * Packed layout (row groups of 64 output features):
+ *   quant plane, NG*KB*2048 bytes: byte ((g*KB + kb)*2 + h)*1024 + r*16 + t
+ *     holds q[64g + r][32kb + 16h + t]   (h in {0,1}, r < 64, t < 16),
+ *   scale plane, right after it, NG*KB*64 binary16 values: element
+ *     (g*KB + kb)*64 + r holds d[64g + r][kb].
+ *   Rows 64g + r >= N are zero.  Each 1 KB piece (g, kb, h) is what one
+ *   64-lane wave loads with one 16-byte load per lane.
+ *
+ * Errors: Q8_ERR_NULL (packed_bytes NULL, or w_blocks NULL when packing),
+ * Q8_ERR_SHAPE, Q8_ERR_ALIGN (w_packed), Q8_ERR_SIZE, Q8_ERR_DEVICE,
+ * Q8_ERR_LAUNCH.
+ */
+q8_status q8_pack_weights(const void *w_blocks, int64_t N, int64_t K,
+                          void *w_packed, size_t *packed_bytes, void *stream);
+
+/*
+ * q8_quantize_act -- quantise activation rows to Q8_0 blocks.
+ *
+ * Operation, per block of 32 values x[0..31] (bfloat16 is widened exactly):
+ *   amax = max |x_j|;  d32 = amax / 127  (binary32, correctly rounded);
+ *   if d32 < FLT_MIN (all-zero and denormal-scale blocks): q = 0, d = +0;
+ *   else id = 1 / d32 (correctly rounded), q_j = x_j * id rounded half
+ *   away from zero, d = binary16(d32) rounded to nearest even.
+ *   (The Q8_0 quantiser; see the source note at the top.)
+ *
+ * x     [M][ldx] binary32 or bfloat16 (dtype); 16-byte aligned and
+ *       ldx*sizeof(elem) % 16 == 0.  Only the first K columns are read.
+ * M     rows (M == 0: nothing is enqueued); K >= 32, K % 32 == 0; ldx >= K.
+ * q     [M][K] int8 out, 16-byte aligned.
+ * d     [M][K/32] binary16 bits out, 2-byte aligned.
+ *
+ * Errors: Q8_ERR_NULL, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DTYPE,
+ * Q8_ERR_DEVICE, Q8_ERR_LAUNCH.
+ */
+q8_status q8_quantize_act(const void *x, q8_dtype dtype, int64_t M, int64_t K,
+                          int64_t ldx, int8_t *q, uint16_t *d, void *stream);
+
+/*
+ * q8_gemm -- C = A * W^T on Q8_0 operands (the formula at the top).
+ *
+ * q_a   [M][K] int8 and d_a [M][K/32] binary16 bits, as written by
+ *       q8_quantize_act; q_a 16-byte aligned, d_a 2-byte aligned.
+ * w_packed  the output of q8_pack_weights for the same N and K.
+ * C     [M][ldc] binary32 out, ldc >= N, 4-byte aligned; overwritten.
+ * M     M == 0 enqueues nothing.  M <= 8 runs the bandwidth-bound
+ *       decode kernel, larger M the int8 matrix-core kernel; both give
+ *       the same value within the bound below.
+ *
+ * Accuracy: every block's int32 dot is exact; each block term is scaled
+ * and accumulated in binary32, so |C - C_exact| <= (K/32 + 2) * 2^-24 *
+ * sum_kb |d_a d_w| sum_j |q_a q_w|.  Results are bitwise reproducible from
+ * run to run for the same inputs and shape.
+ *
+ * Errors: Q8_ERR_NULL, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE,
+ * Q8_ERR_LAUNCH.
+ */
+q8_status q8_gemm(int64_t M, int64_t N, int64_t K,
+                  const int8_t *q_a, const uint16_t *d_a, const void *w_packed,
+                  float *C, int64_t ldc, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *q8_status_string(q8_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q8_H */

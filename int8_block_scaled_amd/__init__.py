@@ -1,0 +1,151 @@
+"""Python binding of libq8gemm: the Q8_0 weight x activation product on MI355X.
+
+Argument marshalling only.  Every step runs in the HIP kernels of
+``libq8gemm.so`` behind the C ABI of ``include/q8.h``; torch supplies device
+memory and the current HIP stream.  There is no CPU fallback: if the library
+is missing or the device is not gfx950 these functions raise.
+
+The calls keep the C names:
+
+* ``q8_pack_weights(w_blocks, N, K)``  GGUF Q8_0 blocks -> packed layout
+* ``q8_quantize_act(x, K=None)``       fp32/bf16 rows -> (int8 q, fp16 d)
+* ``q8_gemm(q_a, d_a, w_packed, N, K)``  C = A W^T in fp32
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq8gemm.so")
+
+Q8_F32, Q8_BF16 = 0, 1
+STATUS = {0: "Q8_OK", 1: "Q8_ERR_NULL", 2: "Q8_ERR_SHAPE", 3: "Q8_ERR_ALIGN",
+          4: "Q8_ERR_DTYPE", 5: "Q8_ERR_SIZE", 6: "Q8_ERR_DEVICE", 7: "Q8_ERR_LAUNCH"}
+EXPORTS = ("q8_pack_weights", "q8_quantize_act", "q8_gemm", "q8_status_string")
+
+_lib = None
+
+
+class Q8Error(RuntimeError):
+    def __init__(self, call, status):
+        self.status = status
+        msg = _load().q8_status_string(status).decode()
+        super().__init__("%s failed: %s (%s)" % (call, STATUS.get(status, status), msg))
+
+
+def _load():
+    """Load libq8gemm.so (built by __graft_entry__.build() or
+    int8_block_scaled_amd/build.py).  Raises if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libq8gemm.so is not built (%s); run "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        L.q8_pack_weights.argtypes = [vp, i64, i64, vp, ctypes.POINTER(sz), vp]
+        L.q8_pack_weights.restype = ctypes.c_int
+        L.q8_quantize_act.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp]
+        L.q8_quantize_act.restype = ctypes.c_int
+        L.q8_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, i64, vp]
+        L.q8_gemm.restype = ctypes.c_int
+        L.q8_status_string.argtypes = [ctypes.c_int]
+        L.q8_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def lib():
+    return _load()
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(call, st):
+    if st != 0:
+        raise Q8Error(call, st)
+
+
+def _need_cuda(name, t):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+
+
+def q8_packed_bytes(N: int, K: int) -> int:
+    """Size of the packed weight buffer for an N x K weight."""
+    n = ctypes.c_size_t(0)
+    _check("q8_pack_weights", _load().q8_pack_weights(None, N, K, None, ctypes.byref(n), None))
+    return n.value
+
+
+def q8_pack_weights(w_blocks: torch.Tensor, N: int, K: int, out: torch.Tensor = None) -> torch.Tensor:
+    """GGUF Q8_0 blocks (uint8, N*K/32*34 bytes, on the GPU) -> packed uint8."""
+    _need_cuda("w_blocks", w_blocks)
+    if w_blocks.dtype != torch.uint8 or not w_blocks.is_contiguous():
+        raise TypeError("w_blocks must be contiguous uint8")
+    if w_blocks.numel() != N * (K // 32) * 34:
+        raise ValueError("w_blocks holds %d bytes, expected N*K/32*34 = %d"
+                         % (w_blocks.numel(), N * (K // 32) * 34))
+    need = q8_packed_bytes(N, K)
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=w_blocks.device)
+    n = ctypes.c_size_t(out.numel())
+    _check("q8_pack_weights", _load().q8_pack_weights(
+        _ptr(w_blocks), N, K, _ptr(out), ctypes.byref(n), _stream(w_blocks)))
+    return out
+
+
+def q8_quantize_act(x: torch.Tensor, K: int = None, q: torch.Tensor = None,
+                    d: torch.Tensor = None):
+    """Rows of x (float32 or bfloat16, [M][ldx], unit column stride) ->
+    (q int8 [M][K], d float16 [M][K/32])."""
+    _need_cuda("x", x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if x.dtype == torch.float32:
+        dt = Q8_F32
+    elif x.dtype == torch.bfloat16:
+        dt = Q8_BF16
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    M = x.shape[0]
+    K = x.shape[1] if K is None else K
+    ldx = x.stride(0) if M > 1 else max(x.stride(0), K)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((M, K // 32), dtype=torch.float16, device=x.device)
+    _check("q8_quantize_act", _load().q8_quantize_act(
+        _ptr(x), dt, M, K, ldx, _ptr(q), _ptr(d), _stream(x)))
+    return q, d
+
+
+def q8_gemm(q_a: torch.Tensor, d_a: torch.Tensor, w_packed: torch.Tensor, N: int, K: int,
+            out: torch.Tensor = None) -> torch.Tensor:
+    """C[M][N] float32 = dequant(q_a, d_a) @ dequant(W)^T for packed W."""
+    for name, t in (("q_a", q_a), ("d_a", d_a), ("w_packed", w_packed)):
+        _need_cuda(name, t)
+    if q_a.dtype != torch.int8 or not q_a.is_contiguous() or q_a.dim() != 2 or q_a.shape[1] != K:
+        raise TypeError("q_a must be contiguous int8 [M][K]")
+    if d_a.dtype not in (torch.float16, torch.int16) or not d_a.is_contiguous() \
+            or tuple(d_a.shape) != (q_a.shape[0], K // 32):
+        raise TypeError("d_a must be contiguous float16 [M][K/32]")
+    if w_packed.numel() < q8_packed_bytes(N, K):
+        raise ValueError("w_packed is smaller than the packed layout for N=%d K=%d" % (N, K))
+    M = q_a.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=q_a.device)
+    if out.dtype != torch.float32 or out.dim() != 2 or out.stride(1) != 1 or out.shape[1] < N \
+            or out.shape[0] != M:
+        raise TypeError("out must be float32 [M][>=N] with unit column stride")
+    ldc = out.stride(0) if M > 1 else max(out.stride(0), N)
+    _check("q8_gemm", _load().q8_gemm(M, N, K, _ptr(q_a), _ptr(d_a), _ptr(w_packed),
+                                      _ptr(out), ldc, _stream(q_a)))
+    return out

@@ -1,0 +1,118 @@
+// q8_api.hip -- the C ABI of libq8gemm (declared and documented in
+// include/q8.h): host-side argument checks, the one-time device check,
+// dispatch and launch.  No allocation, no synchronisation.
+#include <atomic>
+#include <cstring>
+
+#include "q8.h"
+#include "q8_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked yet, 1 = gfx950, 2 = something else
+std::atomic<int> g_device_ok[kMaxDevices];
+
+q8_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q8_ERR_DEVICE;
+  int state = g_device_ok[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return Q8_ERR_DEVICE;
+    state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_ok[dev].store(state, std::memory_order_release);
+  }
+  return state == 1 ? Q8_OK : Q8_ERR_DEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Sizes the kernels index with 32-bit grids and 64-bit offsets: keep every
+// launch's workgroup count below 2^31.
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+bool valid_k(int64_t K) { return K >= 32 && K % 32 == 0 && K < kMaxDim; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* q8_status_string(q8_status s) {
+  switch (s) {
+    case Q8_OK: return "ok";
+    case Q8_ERR_NULL: return "null pointer argument";
+    case Q8_ERR_SHAPE: return "invalid shape (need K % 32 == 0, K >= 32, N >= 1, M >= 0, ld >= row length)";
+    case Q8_ERR_ALIGN: return "misaligned pointer or row pitch";
+    case Q8_ERR_DTYPE: return "unknown dtype";
+    case Q8_ERR_SIZE: return "packed buffer too small";
+    case Q8_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
+    case Q8_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+q8_status q8_pack_weights(const void* w_blocks, int64_t N, int64_t K, void* w_packed,
+                          size_t* packed_bytes, void* stream) {
+  if (packed_bytes == nullptr) return Q8_ERR_NULL;
+  if (N < 1 || N >= kMaxDim || !valid_k(K)) return Q8_ERR_SHAPE;
+  const int64_t NG = q8::num_groups(N);
+  const int64_t KB = K / q8::kQK;
+  const size_t need = static_cast<size_t>(NG * KB) * (q8::kGroupBlockBytes + 2 * q8::kGroupRows);
+  if (w_packed == nullptr) {
+    *packed_bytes = need;
+    return Q8_OK;
+  }
+  if (w_blocks == nullptr) return Q8_ERR_NULL;
+  if (!aligned(w_packed, 16)) return Q8_ERR_ALIGN;
+  if (*packed_bytes < need) return Q8_ERR_SIZE;
+  if (NG * KB * 2 * q8::kGroupRows / 256 >= kMaxDim) return Q8_ERR_SHAPE;
+  const q8_status dev = check_device();
+  if (dev != Q8_OK) return dev;
+  return q8::launch_pack(static_cast<const uint8_t*>(w_blocks), N, K,
+                         static_cast<uint8_t*>(w_packed), as_stream(stream)) == hipSuccess
+             ? Q8_OK
+             : Q8_ERR_LAUNCH;
+}
+
+q8_status q8_quantize_act(const void* x, q8_dtype dtype, int64_t M, int64_t K, int64_t ldx,
+                          int8_t* q, uint16_t* d, void* stream) {
+  if (dtype != Q8_F32 && dtype != Q8_BF16) return Q8_ERR_DTYPE;
+  if (M < 0 || !valid_k(K) || ldx < K) return Q8_ERR_SHAPE;
+  if (M == 0) return Q8_OK;
+  if (x == nullptr || q == nullptr || d == nullptr) return Q8_ERR_NULL;
+  const int64_t esize = dtype == Q8_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(q, 16) || !aligned(d, 2))
+    return Q8_ERR_ALIGN;
+  if (M * (K / q8::kQK) * 4 / 256 >= kMaxDim) return Q8_ERR_SHAPE;
+  const q8_status dev = check_device();
+  if (dev != Q8_OK) return dev;
+  return q8::launch_quantize(x, static_cast<int>(dtype), M, K, ldx, q, d, as_stream(stream)) ==
+                 hipSuccess
+             ? Q8_OK
+             : Q8_ERR_LAUNCH;
+}
+
+q8_status q8_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
+                  const void* w_packed, float* C, int64_t ldc, void* stream) {
+  if (M < 0 || N < 1 || N >= kMaxDim || !valid_k(K) || ldc < N) return Q8_ERR_SHAPE;
+  if (M == 0) return Q8_OK;
+  if (q_a == nullptr || d_a == nullptr || w_packed == nullptr || C == nullptr) return Q8_ERR_NULL;
+  if (!aligned(q_a, 16) || !aligned(d_a, 2) || !aligned(w_packed, 16) || !aligned(C, 4))
+    return Q8_ERR_ALIGN;
+  // workgroup count of the matrix-core kernel: ceil(M/128) * ceil(N/128)
+  if (((M + 127) / 128) * ((N + 127) / 128) >= kMaxDim) return Q8_ERR_SHAPE;
+  const q8_status dev = check_device();
+  if (dev != Q8_OK) return dev;
+  const uint8_t* wp = static_cast<const uint8_t*>(w_packed);
+  hipError_t e;
+  if (M <= q8::kGemvMaxM)
+    e = q8::launch_gemv(static_cast<int>(M), N, K, q_a, d_a, wp, C, ldc, as_stream(stream));
+  else
+    e = q8::launch_gemm(M, N, K, q_a, d_a, wp, C, ldc, as_stream(stream));
+  return e == hipSuccess ? Q8_OK : Q8_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/q8.h declares, and rejects bad arguments on the host before any HIP
+call (so these paths run on a machine with no GPU at all)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int8_block_scaled_amd as q8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8.h")
+
+OK, NULL, SHAPE, ALIGN, DTYPE, SIZE = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return q8.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(q8.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), "libq8gemm.so does not export %s" % n
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.q8_status_string(s)
+    assert L.q8_status_string(99) == b"unknown status"
+
+
+def test_packed_size_query_matches_layout(orc):
+    for N, K in [(1, 32), (64, 512), (70, 96), (12288, 4096), (17408, 5120)]:
+        assert q8.q8_packed_bytes(N, K) == orc.packed_bytes(N, K)
+    assert q8.q8_packed_bytes(12288, 4096) == 12288 * 4096 * 34 // 32
+
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: checks fail first
+ODD = ctypes.c_void_p(0x10001)
+
+
+def test_pack_validation(L):
+    n = ctypes.c_size_t(1 << 40)
+    assert L.q8_pack_weights(FAKE, 64, 512, FAKE, None, None) == NULL
+    assert L.q8_pack_weights(FAKE, 0, 512, FAKE, ctypes.byref(n), None) == SHAPE
+    assert L.q8_pack_weights(FAKE, 64, 48, FAKE, ctypes.byref(n), None) == SHAPE
+    assert L.q8_pack_weights(FAKE, 64, 0, FAKE, ctypes.byref(n), None) == SHAPE
+    assert L.q8_pack_weights(None, 64, 512, FAKE, ctypes.byref(n), None) == NULL
+    assert L.q8_pack_weights(FAKE, 64, 512, ODD, ctypes.byref(n), None) == ALIGN
+    small = ctypes.c_size_t(100)
+    assert L.q8_pack_weights(FAKE, 64, 512, FAKE, ctypes.byref(small), None) == SIZE
+
+
+def test_quantize_validation(L):
+    assert L.q8_quantize_act(FAKE, 2, 4, 64, 64, FAKE, FAKE, None) == DTYPE
+    assert L.q8_quantize_act(FAKE, 0, -1, 64, 64, FAKE, FAKE, None) == SHAPE
+    assert L.q8_quantize_act(FAKE, 0, 4, 48, 64, FAKE, FAKE, None) == SHAPE
+    assert L.q8_quantize_act(FAKE, 0, 4, 64, 32, FAKE, FAKE, None) == SHAPE   # ldx < K
+    assert L.q8_quantize_act(None, 0, 0, 64, 64, None, None, None) == OK      # M == 0: no-op
+    assert L.q8_quantize_act(None, 0, 4, 64, 64, FAKE, FAKE, None) == NULL
+    assert L.q8_quantize_act(ODD, 0, 4, 64, 64, FAKE, FAKE, None) == ALIGN
+    assert L.q8_quantize_act(FAKE, 0, 4, 64, 66, FAKE, FAKE, None) == ALIGN   # pitch 264 B
+    assert L.q8_quantize_act(FAKE, 1, 4, 64, 68, FAKE, FAKE, None) == ALIGN   # pitch 136 B
+    assert L.q8_quantize_act(FAKE, 0, 4, 64, 64, ODD, FAKE, None) == ALIGN
+    assert L.q8_quantize_act(FAKE, 0, 4, 64, 64, FAKE, ODD, None) == ALIGN
+
+
+def test_gemm_validation(L):
+    assert L.q8_gemm(-1, 64, 64, FAKE, FAKE, FAKE, FAKE, 64, None) == SHAPE
+    assert L.q8_gemm(4, 0, 64, FAKE, FAKE, FAKE, FAKE, 64, None) == SHAPE
+    assert L.q8_gemm(4, 64, 65, FAKE, FAKE, FAKE, FAKE, 64, None) == SHAPE
+    assert L.q8_gemm(4, 64, 64, FAKE, FAKE, FAKE, FAKE, 63, None) == SHAPE   # ldc < N
+    assert L.q8_gemm(0, 64, 64, None, None, None, None, 64, None) == OK      # M == 0: no-op
+    assert L.q8_gemm(4, 64, 64, None, FAKE, FAKE, FAKE, 64, None) == NULL
+    assert L.q8_gemm(4, 64, 64, FAKE, None, FAKE, FAKE, 64, None) == NULL
+    assert L.q8_gemm(4, 64, 64, FAKE, FAKE, None, FAKE, 64, None) == NULL
+    assert L.q8_gemm(4, 64, 64, FAKE, FAKE, FAKE, None, 64, None) == NULL
+    assert L.q8_gemm(4, 64, 64, ODD, FAKE, FAKE, FAKE, 64, None) == ALIGN
+    assert L.q8_gemm(4, 64, 64, FAKE, ODD, FAKE, FAKE, 64, None) == ALIGN
+    assert L.q8_gemm(4, 64, 64, FAKE, FAKE, ODD, FAKE, 64, None) == ALIGN
+    assert L.q8_gemm(4, 64, 64, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10002), 64, None) == ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        q8.q8_quantize_act(torch.zeros(4, 64))

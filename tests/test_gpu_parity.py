@@ -1,0 +1,260 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every input is seeded (workloads.py); the oracle quantises the weights into
+GGUF Q8_0 blocks, which both sides then consume.  Activations are quantised
+by both sides and must agree bit for bit before the products are compared.
+"""
+import numpy as np
+import pytest
+import torch
+
+import int8_block_scaled_amd as q8
+import pins
+import workloads
+from gpu_util import DEV, blocks_to_dev, check_close, d_bits, qd_to_dev, say, x_to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+# --------------------------------------------------------------------------
+# quantiser
+# --------------------------------------------------------------------------
+
+def test_quantize_golden_blocks():
+    cases = pins.load_block_cases()
+    x = np.stack([c["x"] for c in cases])
+    say("quantize golden blocks: %d rows x 32 (fp32)" % len(cases))
+    q, d = q8.q8_quantize_act(x_to_dev(x))
+    q, d = q.cpu().numpy(), d_bits(d)
+    for i, c in enumerate(cases):
+        assert np.array_equal(q[i], c["q"]), "%s: q %s" % (c["name"], q[i])
+        assert d[i, 0] == c["d"], "%s: d %#06x" % (c["name"], d[i, 0])
+
+
+def _random_scale_rows(M, K, seed):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((M, K))
+    mag = 2.0 ** r.uniform(-30, 20, (M, K // 32, 1))          # incl. binary16-subnormal scales
+    x = (x.reshape(M, K // 32, 32) * mag).reshape(M, K)
+    ties = r.random((M, K // 32)) < 0.2                       # blocks of half-integers, amax 127
+    for m, kb in zip(*np.nonzero(ties)):
+        blk = np.round(r.uniform(-126, 126, 32) * 2) / 2
+        blk[r.integers(32)] = 127 * r.choice([-1, 1])
+        x[m, 32 * kb:32 * kb + 32] = blk
+    x[:, :32] = 0.0                                            # an all-zero block per row
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_random_scales(orc, dtype):
+    x = _random_scale_rows(64, 1024, 21)
+    if dtype == "bf16":
+        x = workloads.f32_to_bf16_bits(x)
+    say("quantize random scales %s 64x1024" % dtype)
+    q, d = q8.q8_quantize_act(x_to_dev(x))
+    qr, dr = orc.quantize_rows(x)
+    assert np.array_equal(q.cpu().numpy(), qr)
+    assert np.array_equal(d_bits(d), dr)
+
+
+def test_quantize_row_pitch(orc):
+    x = _random_scale_rows(9, 256, 22)
+    K = 160                                                    # read the first 160 of 256 columns
+    say("quantize ldx=256 K=160")
+    xt = x_to_dev(x)
+    q, d = q8.q8_quantize_act(xt, K=K)
+    qr, dr = orc.quantize_rows(x, K=K, ldx=256)
+    assert np.array_equal(q.cpu().numpy(), qr) and np.array_equal(d_bits(d), dr)
+
+
+QUANT_LAYERS = [workloads.TINY, workloads.DECODE_M4, workloads.PREFILL, workloads.LARGE_UP,
+                workloads.LARGE_DOWN] + workloads.sweep(509)[::3]
+
+
+@pytest.mark.parametrize("layer", QUANT_LAYERS, ids=lambda l: l.name)
+def test_quantize_workload_bitexact(orc, layer):
+    x = workloads.activations(layer)
+    say("quantize %s (%s)" % (layer.name, x.dtype))
+    q, d = q8.q8_quantize_act(x_to_dev(x))
+    qr, dr = orc.quantize_rows(x)
+    assert np.array_equal(q.cpu().numpy(), qr), "q differs"
+    assert np.array_equal(d_bits(d), dr), "d differs"
+
+
+@pytest.mark.parametrize("layer", [workloads.TINY, workloads.PREFILL], ids=lambda l: l.name)
+def test_quantize_weights_bitexact(orc, layer):
+    """The same quantiser applied to weight rows (binary32) matches too."""
+    w = workloads.weights(layer)
+    say("quantize weights %s" % layer.name)
+    q, d = q8.q8_quantize_act(x_to_dev(w))
+    qr, dr = orc.quantize_rows(w)
+    assert np.array_equal(q.cpu().numpy(), qr) and np.array_equal(d_bits(d), dr)
+
+
+# --------------------------------------------------------------------------
+# pack
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(64, 32), (70, 96), (256, 512), (130, 1056), (12288, 4096)])
+def test_pack_bitexact(orc, N, K):
+    r = np.random.default_rng(N * 7 + K)
+    q = r.integers(-127, 128, (N, K)).astype(np.int8)
+    d = r.integers(0, 0x7BFF, (N, K // 32)).astype(np.uint16)
+    blocks = orc.blocks_from_qd(q, d)
+    say("pack N=%d K=%d" % (N, K))
+    got = q8.q8_pack_weights(blocks_to_dev(blocks), N, K).cpu().numpy()
+    assert np.array_equal(got, orc.pack(blocks, N, K))
+
+
+# --------------------------------------------------------------------------
+# product: integer exactness, small shapes in full, determinism, guards
+# --------------------------------------------------------------------------
+
+def _problem(M, N, K, seed, unit=False):
+    r = np.random.default_rng(seed)
+    qa = r.integers(-127, 128, (M, K)).astype(np.int8)
+    qw = r.integers(-127, 128, (N, K)).astype(np.int8)
+    if unit:
+        da = np.full((M, K // 32), 0x3C00, np.uint16)
+        dw = np.full((N, K // 32), 0x3C00, np.uint16)
+    else:
+        da = (np.abs(r.standard_normal((M, K // 32))) * 0.02 + 1e-3).astype(np.float16).view(np.uint16)
+        dw = (np.abs(r.standard_normal((N, K // 32))) * 5e-4 + 1e-5).astype(np.float16).view(np.uint16)
+    return qa, da, qw, dw
+
+
+def _run(qa, da, blocks, N, K, out=None):
+    qt, dt = qd_to_dev(qa, da)
+    wp = q8.q8_pack_weights(blocks_to_dev(blocks), N, K)
+    C = q8.q8_gemm(qt, dt, wp, N, K, out=out)
+    torch.cuda.synchronize()
+    return C
+
+
+@pytest.mark.parametrize("K", [32, 64, 512, 1024])
+@pytest.mark.parametrize("M", [1, 4, 8, 9, 16, 130])
+def test_gemm_unit_scale_is_exact_integer(orc, M, K):
+    """All scales 1.0 and K <= 1024: C is an integer below 2^24, so every
+    block's int32 dot must come out exactly."""
+    N = 200
+    qa, da, qw, dw = _problem(M, N, K, 1000 + M * 31 + K, unit=True)
+    say("unit-scale gemm M=%d N=%d K=%d" % (M, N, K))
+    C = _run(qa, da, orc.blocks_from_qd(qw, dw), N, K).cpu().numpy()
+    want = (qa.astype(np.int64) @ qw.astype(np.int64).T).astype(np.float64)
+    assert np.array_equal(C.astype(np.float64), want)
+
+
+SMALL_SHAPES = [(M, 256, 512) for M in range(1, 10)] + [
+    (16, 256, 512), (17, 70, 96), (33, 130, 160), (127, 200, 544), (128, 128, 128),
+    (129, 64, 32), (255, 257, 1056), (300, 330, 2080), (509, 640, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL_SHAPES)
+def test_gemm_parity_small(orc, M, N, K):
+    qa, da, qw, dw = _problem(M, N, K, 7 * M + 13 * N + K)
+    say("gemm parity M=%d N=%d K=%d" % (M, N, K))
+    C = _run(qa, da, orc.blocks_from_qd(qw, dw), N, K).cpu().numpy()
+    C_ref, absdot = orc.gemm(qa, da, qw, dw)
+    check_close(C, C_ref, absdot, K, "M%d N%d K%d" % (M, N, K))
+
+
+def test_gemm_tiny_workload_every_m(orc):
+    """The tiny workload, through the quantiser, at every M from 1 to 16
+    (1..8 take the decode kernel, 9..16 the matrix-core kernel)."""
+    layer = workloads.TINY
+    N, K = layer.N, layer.K
+    x = workloads.activations(layer)
+    qw, dw = orc.quantize_rows(workloads.weights(layer))
+    say("tiny workload M=1..16")
+    wp = q8.q8_pack_weights(blocks_to_dev(orc.blocks_from_qd(qw, dw)), N, K)
+    qa_t, da_t = q8.q8_quantize_act(x_to_dev(x))
+    qa, da = orc.quantize_rows(x)
+    assert np.array_equal(qa_t.cpu().numpy(), qa) and np.array_equal(d_bits(da_t), da)
+    C_ref, absdot = orc.gemm(qa, da, qw, dw)
+    for M in range(1, layer.M + 1):
+        C = q8.q8_gemm(qa_t[:M].contiguous(), da_t[:M].contiguous(), wp, N, K).cpu().numpy()
+        check_close(C, C_ref[:M], absdot[:M], K, "tiny M=%d" % M)
+
+
+@pytest.mark.parametrize("M", [3, 300])
+def test_gemm_guard_bands(orc, M):
+    """Columns past N (ldc > N) and rows past M are never written."""
+    N, K, ldc, extra = 70, 160, 96, 5
+    qa, da, qw, dw = _problem(M, N, K, 77 + M)
+    say("guard bands M=%d N=%d ldc=%d" % (M, N, ldc))
+    out = torch.full((M + extra, ldc), float("nan"), dtype=torch.float32, device=DEV)
+    view = out[:M]
+    C = _run(qa, da, orc.blocks_from_qd(qw, dw), N, K, out=view)
+    assert C.data_ptr() == out.data_ptr()
+    host = out.cpu().numpy()
+    assert np.all(np.isnan(host[:, N:])), "wrote past column N"
+    assert np.all(np.isnan(host[M:])), "wrote past row M"
+    C_ref, absdot = orc.gemm(qa, da, qw, dw)
+    check_close(host[:M, :N], C_ref, absdot, K, "guarded")
+
+
+@pytest.mark.parametrize("M", [4, 512])
+def test_gemm_deterministic(orc, M):
+    N, K = 4096, 4096
+    qa, da, qw, dw = _problem(M, N, K, 99 + M)
+    say("determinism M=%d N=%d K=%d" % (M, N, K))
+    qt, dt = qd_to_dev(qa, da)
+    wp = q8.q8_pack_weights(blocks_to_dev(orc.blocks_from_qd(qw, dw)), N, K)
+    C1 = q8.q8_gemm(qt, dt, wp, N, K)
+    C2 = q8.q8_gemm(qt, dt, wp, N, K)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int32), C2.view(torch.int32))
+
+
+def test_gemm_m_zero():
+    say("gemm M=0")
+    qt = torch.empty((0, 64), dtype=torch.int8, device=DEV)
+    dt = torch.empty((0, 2), dtype=torch.float16, device=DEV)
+    wp = torch.zeros(q8.q8_packed_bytes(64, 64), dtype=torch.uint8, device=DEV)
+    C = q8.q8_gemm(qt, dt, wp, 64, 64)
+    assert C.shape == (0, 64)
+
+
+# --------------------------------------------------------------------------
+# the workloads at full size
+# --------------------------------------------------------------------------
+
+FULL_LAYERS = [workloads.DECODE_M1, workloads.DECODE_M4, workloads.PREFILL, workloads.LARGE_UP,
+               workloads.LARGE_DOWN] + workloads.sweep(512) + workloads.sweep(509)
+
+
+def _sample_points(M, N, n, seed):
+    r = np.random.default_rng(seed)
+    rows = [r.integers(0, M, n)]
+    cols = [r.integers(0, N, n)]
+    for m in sorted({0, M - 1}):                      # two whole rows (first/last tile)
+        rows.append(np.full(N, m))
+        cols.append(np.arange(N))
+    for c in sorted({0, N - 1}):                      # two whole columns
+        rows.append(np.arange(M))
+        cols.append(np.full(M, c))
+    return np.concatenate(rows), np.concatenate(cols)
+
+
+@pytest.mark.parametrize("layer", FULL_LAYERS, ids=lambda l: l.name)
+def test_workload_full_size(orc, layer):
+    M, N, K = layer.M, layer.N, layer.K
+    say("full size %s: generating" % layer.name)
+    x = workloads.activations(layer)
+    qw, dw = orc.quantize_rows(workloads.weights(layer))
+    qa, da = orc.quantize_rows(x)
+    say("full size %s: GPU quantise + pack + gemm" % layer.name)
+    wp = q8.q8_pack_weights(blocks_to_dev(orc.blocks_from_qd(qw, dw)), N, K)
+    qa_t, da_t = q8.q8_quantize_act(x_to_dev(x))
+    C = q8.q8_gemm(qa_t, da_t, wp, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(qa_t.cpu().numpy(), qa), "quantised activations differ"
+    assert np.array_equal(d_bits(da_t), da), "activation scales differ"
+    if M * N * K <= 4 * 12288 * 4096:
+        C_ref, absdot = orc.gemm(qa, da, qw, dw)
+        check_close(C.cpu().numpy(), C_ref, absdot, K, layer.name)
+    else:
+        rows, cols = _sample_points(M, N, 4096, M + N + K)
+        C_ref, absdot = orc.gemm_sampled(qa, da, qw, dw, rows, cols)
+        got = C[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)].cpu().numpy()
+        check_close(got, C_ref, absdot, K, layer.name)
