@@ -1,0 +1,229 @@
+"""Benchmark of the Q8_0 weight x activation product on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  prefill: q8_quantize_act (bf16 2048 x 4096) + q8_gemm (M2048 N12288 K4096)
+  decode : q8_quantize_act + q8_gemm at M=1 and at M=4 (N12288 K4096)
+Weights are packed once (not timed).  Packed weight copies are rotated from
+step to step over more than the 256 MB MALL, so weights come from HBM.
+
+value  = prefill throughput, 2*M*N*K / (quantise + GEMM time), in TOPS
+         (int8 multiply-adds counted as 2 ops).
+roofline = the prefill GEMM kernel alone, timed with HIP events around each
+         launch on the stream it runs on, against the 5.0 POP/s dense int8
+         matrix-core peak.  "decode" carries the same for the M=1 and M=4
+         kernels against 8 TB/s HBM.
+cpu_baseline = the CPU oracle (oracle/q8ref.c, OpenMP) on the host cores,
+         timed on a bounded sample of the same prefill product.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Q8_0 GEMM TOPS @M=2048 (% int8 MFMA peak) + decode GEMV GB/s (% HBM)"
+PEAK_INT8_TOPS = 5000.0          # MI355X dense int8 matrix-core peak, TOP/s
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--rotate", type=int, default=8, help="packed weight copies cycled over")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_sha(name):
+    path = os.path.join(ROOT, "int8_block_scaled_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(profile_name, source, per_launch_bytes_alg):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, profile_name)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha") != kernel_source_sha(source):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        sys.exit("bench.py measures one GPU: this build has no multi-GPU path "
+                 "(the product shards by N or M with no communication; see DESIGN.md). "
+                 "Run with --gpus 1.")
+
+    import numpy as np
+    import torch
+
+    import int8_block_scaled_amd as q8
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pre, dec1, dec4 = workloads.PREFILL, workloads.DECODE_M1, workloads.DECODE_M4
+    N, K = pre.N, pre.K
+    assert (dec1.N, dec1.K) == (N, K)
+
+    # ---- inputs (seeded, synthetic), weights quantised and packed on the GPU
+    w = torch.from_numpy(workloads.weights(pre)).to(dev)
+    qw, dw = q8.q8_quantize_act(w)
+    del w
+    blocks = torch.cat([dw.view(torch.uint8).view(N, K // 32, 2),
+                        qw.view(torch.uint8).view(N, K // 32, 32)], dim=2).contiguous().view(-1)
+    del qw, dw
+    packed0 = q8.q8_pack_weights(blocks, N, K)
+    del blocks
+    packs = [packed0] + [packed0.clone() for _ in range(args.rotate - 1)]
+    xp = torch.from_numpy(workloads.activations(pre).view(np.int16)).to(dev).view(torch.bfloat16)
+    x4 = torch.from_numpy(workloads.activations(dec4).view(np.int16)).to(dev).view(torch.bfloat16)
+    x1 = x4[:1]
+    M = pre.M
+    qa = torch.empty((M, K), dtype=torch.int8, device=dev)
+    da = torch.empty((M, K // 32), dtype=torch.float16, device=dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    q4 = torch.empty((4, K), dtype=torch.int8, device=dev)
+    d4 = torch.empty((4, K // 32), dtype=torch.float16, device=dev)
+    q1 = torch.empty((1, K), dtype=torch.int8, device=dev)
+    d1 = torch.empty((1, K // 32), dtype=torch.float16, device=dev)
+    C4 = torch.empty((4, N), dtype=torch.float32, device=dev)
+    C1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+
+    names = ["quant_prefill", "gemm_prefill", "quant_dec1", "gemv_dec1", "quant_dec4", "gemv_dec4"]
+
+    def step(i, ev=None):
+        wp = packs[i % len(packs)]
+        calls = [
+            lambda: q8.q8_quantize_act(xp, q=qa, d=da),
+            lambda: q8.q8_gemm(qa, da, wp, N, K, out=C),
+            lambda: q8.q8_quantize_act(x1, q=q1, d=d1),
+            lambda: q8.q8_gemm(q1, d1, packs[(i + 3) % len(packs)], N, K, out=C1),
+            lambda: q8.q8_quantize_act(x4, q=q4, d=d4),
+            lambda: q8.q8_gemm(q4, d4, packs[(i + 5) % len(packs)], N, K, out=C4),
+        ]
+        for j, c in enumerate(calls):
+            if ev is not None:
+                ev[j][0].record()
+            c()
+            if ev is not None:
+                ev[j][1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in names]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    dur = {n: np.array([events[i][j][0].elapsed_time(events[i][j][1]) for i in range(args.steps)])
+           for j, n in enumerate(names)}                      # ms per launch
+    mean = {n: float(np.mean(v)) for n, v in dur.items()}
+
+    ops = 2.0 * M * N * K
+    t_pre = (mean["quant_prefill"] + mean["gemm_prefill"]) * 1e-3
+    value = ops / t_pre / 1e12
+    gemm_tops = ops / (mean["gemm_prefill"] * 1e-3) / 1e12
+
+    KB = K // 32
+    w_bytes = N * KB * 34
+
+    def gemv_bytes(m):
+        return w_bytes + m * KB * 34 + 4 * m * N
+
+    dec = {}
+    for m, key in ((1, "gemv_dec1"), (4, "gemv_dec4")):
+        gbs = gemv_bytes(m) / (mean[key] * 1e-3) / 1e9
+        dec["M%d" % m] = {"gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                          "kernel_us": round(mean[key] * 1e3, 2),
+                          "algorithmic_bytes": gemv_bytes(m),
+                          "quantize_us": round(mean[key.replace("gemv", "quant")] * 1e3, 2),
+                          "traffic": measured_traffic("gemv_decode_M%d_traffic.json" % m,
+                                                      "q8_gemv.hip", gemv_bytes(m))}
+
+    roofline = {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS,
+                "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                "traffic": measured_traffic("gemm_prefill_M2048_traffic.json", "q8_gemm.hip",
+                                            None),
+                "kernel": "gemm_q8_mfma_kernel", "kernel_us": round(mean["gemm_prefill"] * 1e3, 2),
+                "algorithmic_ops_per_launch": ops,
+                "epilogue_ceiling_frac": 0.25}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_seconds, qa, da, packs, N, K)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic (seeded N(0,1) bf16 activations, N(0,0.02) weights as Q8_0)",
+        "config": {"workload": "prefill M2048 N12288 K4096 (+ decode M1 and M4, N12288 K4096)",
+                   "M": M, "N": N, "K": K, "act_dtype": "bf16", "weights": "Q8_0",
+                   "weight_copies_rotated": len(packs),
+                   "gemm_only_tops": round(gemm_tops, 1),
+                   "quantize_prefill_us": round(mean["quant_prefill"] * 1e3, 2)},
+        "roofline": roofline,
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(seconds, qa_t, da_t, packs, N, K):
+    """The oracle (plain C, OpenMP over rows) on a bounded row sample of the
+    prefill product; rows are added until about ``seconds`` of CPU time."""
+    import numpy as np
+    import oracle
+
+    orc = oracle.default()
+    import torch
+
+    qa = qa_t.cpu().numpy()
+    da = da_t.cpu().view(torch.int16).numpy().view(np.uint16)
+    # unpack the weights from the packed layout on the host (marshalling only)
+    KB, NG = K // 32, (N + 63) // 64
+    pk = packs[0].cpu().numpy()
+    qplane = pk[:NG * KB * 2048].reshape(NG, KB, 2, 64, 16).view(np.int8)
+    qw = np.ascontiguousarray(qplane.transpose(0, 3, 1, 2, 4).reshape(NG * 64, K)[:N])
+    dw = np.ascontiguousarray(pk[NG * KB * 2048:].view(np.uint16).reshape(NG, KB, 64)
+                              .transpose(0, 2, 1).reshape(NG * 64, KB)[:N])
+    rows, elapsed, chunk = 0, 0.0, 4
+    while elapsed < seconds and rows < qa.shape[0]:
+        r1 = min(qa.shape[0], rows + chunk)
+        t0 = time.perf_counter()
+        orc.gemm(qa[rows:r1], da[rows:r1], qw, dw)
+        elapsed += time.perf_counter() - t0
+        rows = r1
+        chunk = min(chunk * 2, 64)
+    ops = 2.0 * rows * N * K
+    return {"value": round(ops / elapsed / 1e12, 6), "unit": "TOPS", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": "prefill product rows 0..%d of 2048 (N12288 K4096), %.1f s" % (rows, elapsed)}
+
+
+if __name__ == "__main__":
+    main()

@@ -73,8 +73,8 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(
 #pragma unroll
   for (int m = 0; m < MR; ++m) red[wave][m][lane] = acc[m];
   __syncthreads();
-  const int t = threadIdx.x;
-  if (t < MR * 64) {
+  // MR*64 sums; a workgroup may have fewer than MR waves when KB is small.
+  for (int t = threadIdx.x; t < MR * 64; t += blockDim.x) {
     const int m = t >> 6, r = t & 63;
     float sum = 0.0f;
     for (int w = 0; w < nwaves; ++w) sum += red[w][m][r];
