@@ -43,8 +43,8 @@ extern "C" {
 typedef enum {
     Q8_OK = 0,
     Q8_ERR_NULL = 1,    /* a required pointer is NULL                        */
-    Q8_ERR_SHAPE = 2,   /* K <= 0 or K % 32 != 0, N <= 0, M < 0, ldx < K,
-                           ldc < N, or a size too large for the kernels      */
+    Q8_ERR_SHAPE = 2,   /* K < 32, K % 32 != 0, K > 2^24, N <= 0, M < 0,
+                           ldx < K, ldc < N, or a grid too large to launch  */
     Q8_ERR_ALIGN = 3,   /* a pointer or a row pitch breaks the stated alignment */
     Q8_ERR_DTYPE = 4,   /* unknown q8_dtype                                  */
     Q8_ERR_SIZE = 5,    /* *packed_bytes smaller than the packed layout      */
@@ -66,7 +66,7 @@ typedef enum {
  * w_blocks  [N][K/32] blocks of 34 bytes: binary16 d (little-endian), then
  *           int8 q[32]; block (n, kb) at byte (n*(K/32) + kb)*34.  Any
  *           alignment.
- * N, K      output features and reduction length; N >= 1, K >= 32,
+ * N, K      output features and reduction length; N >= 1, 32 <= K <= 2^24,
  *           K % 32 == 0.
  * w_packed  device buffer, 16-byte aligned, or NULL to query the size.
  * packed_bytes  in: capacity of w_packed; out (when w_packed is NULL): the
@@ -100,7 +100,8 @@ q8_status q8_pack_weights(const void *w_blocks, int64_t N, int64_t K,
  *
  * x     [M][ldx] binary32 or bfloat16 (dtype); 16-byte aligned and
  *       ldx*sizeof(elem) % 16 == 0.  Only the first K columns are read.
- * M     rows (M == 0: nothing is enqueued); K >= 32, K % 32 == 0; ldx >= K.
+ * M     rows (M == 0: nothing is enqueued); 32 <= K <= 2^24, K % 32 == 0;
+ *       ldx >= K.
  * q     [M][K] int8 out, 16-byte aligned.
  * d     [M][K/32] binary16 bits out, 2-byte aligned.
  *

@@ -12,6 +12,7 @@ The calls keep the C names:
 * ``q8_gemm(q_a, d_a, w_packed, N, K)``  C = A W^T in fp32
 """
 import ctypes
+import functools
 import os
 
 import torch
@@ -78,6 +79,7 @@ def _need_cuda(name, t):
         raise TypeError("%s must be a CUDA (HIP) tensor" % name)
 
 
+@functools.lru_cache(maxsize=256)
 def q8_packed_bytes(N: int, K: int) -> int:
     """Size of the packed weight buffer for an N x K weight."""
     n = ctypes.c_size_t(0)

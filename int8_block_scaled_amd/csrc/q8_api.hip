@@ -32,7 +32,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // launch's workgroup count below 2^31.
 constexpr int64_t kMaxDim = int64_t(1) << 31;
 
-bool valid_k(int64_t K) { return K >= 32 && K % 32 == 0 && K < kMaxDim; }
+// K is bounded so that 32-bit buffer offsets cover a 256-row tile of q_a.
+constexpr int64_t kMaxK = int64_t(1) << 24;
+
+bool valid_k(int64_t K) { return K >= 32 && K % 32 == 0 && K <= kMaxK; }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 

@@ -18,25 +18,37 @@
 //     y   = fma(Pbits, d_w, -1.5*2^23*d_w)   = RN(P * d_w)     (one rounding)
 //     acc = fma(y, d_a, acc)                                     (one rounding)
 // i.e. two VALU operations per output and block, with no int->float
-// conversion.  d_w is per lane (lane = output column) and -1.5*2^23*d_w is
-// exact (d_w has 11 significant bits).  With unpacked binary32 FMAs (16
-// lanes per clock per SIMD) against 1024 int8 MACs per clock per SIMD this
-// epilogue caps the kernel at 1/4 of the int8 matrix-core peak; the kernel
-// is organised to keep the VALU busy and everything else off it.
+// conversion.  d_w is per lane (lane = output column); the pair
+// (d_w, -1.5*2^23*d_w) is prepared once per block when staged (the product
+// is exact: d_w has 11 significant bits).  With unpacked binary32 FMAs (16
+// lanes per clock per SIMD) against 1024 int8 MACs per clock per SIMD, this
+// epilogue caps the kernel at 1/4 of the int8 matrix-core peak, so the
+// kernel is built to keep the VALU issuing epilogue FMAs and little else.
 //
-// Tiling.  A workgroup of 4 waves computes a BM x BN = 128 x 128 tile; each
-// wave a 64 x 64 sub-tile (2 x 2 MFMA tiles).  K advances in stages of
-// KBS = 4 blocks.  Per stage, q_a rows, packed weight pieces and both scale
-// vectors are staged HBM -> registers -> LDS, double buffered, so global
-// loads of stage s+1 are in flight while stage s computes.  LDS holds each
-// operand as 16-byte slices in [block][half][row] order, so a fragment load
-// (lane l: row l%32, half l/32) reads 512 contiguous bytes per half-wave.
-// Activation scales are widened to binary32 once, when staged.
+// Data movement.  A workgroup of WAVES_M x WAVES_N waves owns a BM x BN
+// output tile; K advances in stages of KBS blocks through two LDS buffers.
+// Quant tiles go HBM -> LDS with buffer_load ... lds (no registers, no LDS
+// stores), through buffer resources that end at the last valid activation
+// row and packed weight group, so ragged edges read as zero without
+// branches.  Scales come through registers (to be widened to binary32) and
+// are stored after the stage's arithmetic.  LDS holds each operand as
+// 16-byte slices in [block][half][row] order, so a fragment load (lane l:
+// row l%32, half l/32) reads 512 contiguous bytes per half-wave.
+//
+// LDS reads are inline asm with immediate offsets: the compiler cannot tell
+// a read of one stage buffer from the asynchronous loads into the other and
+// would wait for those before every read; the buffer a stage reads is
+// complete once the stage's barrier has passed (every wave waits for its own
+// loads before it).  The reads' completion is awaited explicitly before
+// their values are used, and the asm carries a memory clobber.
 //
 // Workgroup order: tiles run M-fastest so consecutive workgroups share a
 // weight tile; when the grid is a multiple of 8 the ids are remapped so
 // each of the 8 XCDs (which receive workgroups round-robin) gets one
 // contiguous range of tiles and keeps its weight tiles in its own L2.
+#include <cstdlib>
+#include <utility>
+
 #include "q8_kernels.h"
 
 namespace q8 {
@@ -44,124 +56,280 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
-
-constexpr int BM = 128, BN = 128, KBS = 4;
-constexpr int kWaves = 4, kThreads = kWaves * 64;
-constexpr int WM = 64, WN = 64;                 // per-wave tile
-constexpr int TM = WM / 32, TN = WN / 32;       // MFMA tiles per wave
-constexpr int kSlots = 2 * KBS;                 // 16-byte slots per row per stage
-
-// LDS per stage (bytes)
-constexpr int kAq = KBS * 2 * BM * 16;          // activation quants
-constexpr int kBq = KBS * 2 * BN * 16;          // weight quants
-constexpr int kAs = KBS * BM * 4;               // activation scales (binary32)
-constexpr int kBs = KBS * BN * 4;               // weight scales (binary32)
-constexpr int kStage = kAq + kBq + kAs + kBs;
-
-constexpr int kALoads = BM * kSlots / kThreads;         // 16-byte A loads per thread
-constexpr int kBLoads = BN * kSlots / kThreads;         // 16-byte B loads per thread
-constexpr int kASc = BM * KBS / kThreads;               // A scales per thread
-constexpr int kBSc = BN * KBS / kThreads;               // B scales per thread
-static_assert(kALoads * kThreads == BM * kSlots, "A staging");
-static_assert(kBLoads * kThreads == BN * kSlots, "B staging");
-static_assert(kASc * kThreads == BM * KBS && kBSc * kThreads == BN * KBS, "scale staging");
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr float kBias = 12582912.0f;            // 1.5 * 2^23
-constexpr int kBiasBits = 0x4B400000;
+constexpr int kBiasBits = 0x4B400000;           // its binary32 bits
+constexpr uint32_t kOutOfRange = 0xFFFFFFFFu;   // buffer offset that reads as zero
 
-struct Staged {
-  uint4 a[kALoads];
-  uint4 b[kBLoads];
-  float as[kASc];
-  float bs[kBSc];
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int KBS_, int NBUF_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, KBS = KBS_;
+  static constexpr int NBUF = NBUF_;                           // LDS stage buffers
+  static constexpr int kThreads = WAVES_M * WAVES_N * 64;
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // per-wave tile
+  static constexpr int TM = WM / 32, TN = WN / 32;             // MFMA tiles per wave
+  static constexpr int kSlots = 2 * KBS;                       // 16-byte slots per row per stage
+  // LDS per stage (bytes)
+  static constexpr int kAq = KBS * 2 * BM * 16;                // activation quants [kb][h][row]
+  static constexpr int kBq = KBS * 2 * BN * 16;                // weight quants [kb][h][col]
+  static constexpr int kAs = KBS * BM * 4;                     // d_a [kb][row], binary32
+  static constexpr int kBs = KBS * BN * 8;                     // (d_w, -1.5*2^23*d_w) [kb][col]
+  static constexpr int kStage = kAq + kBq + kAs + kBs;
+  // loads per wave per stage, scales per thread per stage
+  static constexpr int kAInst = BM * kSlots / 64 / kWaves;
+  static constexpr int kBInst = (BN / kGroupRows) * 2 * KBS / kWaves;
+  static constexpr int kASc = (BM * KBS + kThreads - 1) / kThreads;
+  static constexpr int kBSc = (BN * KBS + kThreads - 1) / kThreads;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(BN % kGroupRows == 0, "BN must cover whole 64-row groups");
+  static_assert(BM % 64 == 0, "activation loads cover 64 rows each");
+  static_assert(kAInst * 64 * kWaves == BM * kSlots, "activation loads split over waves");
+  static_assert(kBInst * kWaves == (BN / kGroupRows) * 2 * KBS, "weight loads split over waves");
+  static_assert(NBUF >= 2 && NBUF * kStage <= 160 * 1024, "LDS");
+  // VMEM instructions per stage: quant loads per wave, scale loads per thread
+  static constexpr int kDmaOps = kAInst + kBInst;
+  static constexpr int kScaleOps = kASc + kBSc;
+  // Loads issued after a stage's quant loads by the time that stage is
+  // waited for (see the stage loop).
+  static constexpr int kInFlight = (NBUF - 1) * kScaleOps + (NBUF - 2) * kDmaOps;
+  static_assert(kInFlight < 64, "vmcnt range");
+  static_assert(kStage < 65536, "immediate LDS offsets");
 };
 
-__device__ __forceinline__ void load_stage(Staged& st, int tid, int64_t m0, int64_t g0,
-                                           int64_t kb0, int64_t M, int64_t K, int64_t KB,
-                                           int64_t NG, const int8_t* __restrict__ q_a,
-                                           const uint16_t* __restrict__ d_a,
-                                           const uint8_t* __restrict__ wq,
-                                           const uint16_t* __restrict__ ws) {
+// ---------------------------------------------------------------------------
+// compile-time loops and LDS access
+// ---------------------------------------------------------------------------
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_ptr)(const_cast<void*>(p))));
+}
+
+template <int OFF>
+__device__ __forceinline__ v4i lds_read_b128(uint32_t base) {
+  v4i v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(base), "i"(OFF));
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ v2f lds_read_b64(uint32_t base) {
+  v2f v;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(base), "i"(OFF));
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ void lds_write_b32(uint32_t base, float v) {
+  asm volatile("ds_write_b32 %0, %1 offset:%2" : : "v"(base), "v"(v), "i"(OFF) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void lds_write_b64(uint32_t base, v2f v) {
+  asm volatile("ds_write_b64 %0, %1 offset:%2" : : "v"(base), "v"(v), "i"(OFF) : "memory");
+}
+__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Ties a value to the preceding wait so that no use of it moves above it.
+template <class V>
+__device__ __forceinline__ void after_wait(V& v) { asm volatile("" : "+v"(v)); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer: stride 0, range check against num_records (bytes)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// ---------------------------------------------------------------------------
+// per-workgroup state
+// ---------------------------------------------------------------------------
+
+struct Rsrc {
+  __amdgpu_buffer_rsrc_t ra;    // q_a rows [m0, m0 + rows_valid)
+  __amdgpu_buffer_rsrc_t rb;    // packed quant pieces of the tile's row groups
+  __amdgpu_buffer_rsrc_t rsa;   // d_a rows [m0, m0 + rows_valid)
+  __amdgpu_buffer_rsrc_t rsb;   // weight scales of the tile's row groups
+  int KB;
+};
+
+// Issue one stage's quant tiles: HBM -> LDS, no registers.  Per-lane
+// offsets are recomputed each stage (a few integer operations) rather than
+// held in registers across the stage's arithmetic.
+template <class T>
+__device__ __forceinline__ void issue_quants(const Rsrc& r, int wave, int lane, int K, int kb0,
+                                             uint8_t* buf) {
+#if __HIP_DEVICE_COMPILE__   // the buffer builtins exist only in the device pass
+  constexpr int BM = T::BM, BN = T::BN, KBS = T::KBS;
+  kb0 = __builtin_amdgcn_readfirstlane(kb0);   // wave-uniform: the loads' scalar offsets
+  asm volatile("" : "+v"(lane));               // opaque: do not hoist the offsets below
 #pragma unroll
-  for (int i = 0; i < kALoads; ++i) {
-    const int idx = i * kThreads + tid;
-    const int m = (idx & 15) + 16 * (idx >> 7);
-    const int s = (idx >> 4) & (kSlots - 1);
-    const int64_t row = m0 + m, kb = kb0 + (s >> 1);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (row < M && kb < KB)
-      v = *reinterpret_cast<const uint4*>(q_a + row * K + kb0 * kQK + s * 16);
-    st.a[i] = v;
+  for (int u0 = 0; u0 < T::kAInst; ++u0) {
+    const int u = wave * T::kAInst + u0;
+    const int s = u / (BM / 64), mb = u % (BM / 64);
+    const uint32_t voff = static_cast<uint32_t>((mb * 64 + lane) * K + s * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ra, (lds_void_ptr)(buf + (s * BM + mb * 64) * 16),
+                                             16, voff, static_cast<uint32_t>(kb0 * kQK), 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < kBLoads; ++i) {
-    const int idx = i * kThreads + tid;
-    const int piece = idx >> 6, lane = idx & 63;
-    const int gl = piece / (2 * KBS);
-    const int kbl = (piece >> 1) % KBS;
-    const int h = piece & 1;
-    const int64_t g = g0 + gl, kb = kb0 + kbl;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (g < NG && kb < KB)
-      v = reinterpret_cast<const uint4*>(wq + ((g * KB + kb) * 2 + h) * kPieceBytes)[lane];
-    st.b[i] = v;
+  for (int u0 = 0; u0 < T::kBInst; ++u0) {
+    const int u = wave * T::kBInst + u0;
+    const int gl = u / (2 * KBS), kbl = (u >> 1) % KBS, h = u & 1;
+    const uint32_t voff =
+        static_cast<uint32_t>(((gl * r.KB + kbl) * 2 + h) * kPieceBytes + lane * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r.rb, (lds_void_ptr)(buf + T::kAq + ((kbl * 2 + h) * BN + gl * kGroupRows) * 16), 16,
+        voff, static_cast<uint32_t>(kb0 * kGroupBlockBytes), 0, 0);
   }
+#endif
+}
+
+// Load one stage's binary16 scales into registers (blocks past K/32 read as
+// zero through an out-of-range offset).
+template <class T>
+__device__ __forceinline__ void load_scales(const Rsrc& r, int tid, int kb0,
+                                            uint16_t (&as_r)[T::kASc], uint16_t (&bs_r)[T::kBSc]) {
+#if __HIP_DEVICE_COMPILE__
+  constexpr int BM = T::BM, BN = T::BN, KBS = T::KBS;
+  kb0 = __builtin_amdgcn_readfirstlane(kb0);
+  asm volatile("" : "+v"(tid));
 #pragma unroll
-  for (int i = 0; i < kASc; ++i) {
-    const int idx = i * kThreads + tid;
+  for (int i = 0; i < T::kASc; ++i) {
+    const int idx = i * T::kThreads + tid;
     const int m = idx % BM, kbl = idx / BM;
-    const int64_t row = m0 + m, kb = kb0 + kbl;
-    st.as[i] = (row < M && kb < KB) ? f16_bits_to_f32(d_a[row * KB + kb]) : 0.0f;
+    const bool in = idx < BM * KBS && kb0 + kbl < r.KB;
+    const uint32_t off = in ? static_cast<uint32_t>((m * r.KB + kbl) * 2) : kOutOfRange;
+    as_r[i] = __builtin_amdgcn_raw_buffer_load_b16(r.rsa, off, static_cast<uint32_t>(kb0 * 2), 0);
   }
 #pragma unroll
-  for (int i = 0; i < kBSc; ++i) {
-    const int idx = i * kThreads + tid;
+  for (int i = 0; i < T::kBSc; ++i) {
+    const int idx = i * T::kThreads + tid;
     const int n = idx % BN, kbl = idx / BN;
-    const int64_t g = g0 + n / kGroupRows, kb = kb0 + kbl;
-    st.bs[i] = (g < NG && kb < KB) ? f16_bits_to_f32(ws[(g * KB + kb) * kGroupRows + n % kGroupRows])
-                                   : 0.0f;
+    const bool in = idx < BN * KBS && kb0 + kbl < r.KB;
+    const uint32_t off =
+        in ? static_cast<uint32_t>((((n / kGroupRows) * r.KB + kbl) * kGroupRows + n % kGroupRows) * 2)
+           : kOutOfRange;
+    bs_r[i] = __builtin_amdgcn_raw_buffer_load_b16(r.rsb, off,
+                                                   static_cast<uint32_t>(kb0 * kGroupRows * 2), 0);
   }
+#endif
 }
 
-__device__ __forceinline__ void store_stage(const Staged& st, int tid, uint8_t* buf) {
-  uint4* aq = reinterpret_cast<uint4*>(buf);
-  uint4* bq = reinterpret_cast<uint4*>(buf + kAq);
-  float* as = reinterpret_cast<float*>(buf + kAq + kBq);
-  float* bs = reinterpret_cast<float*>(buf + kAq + kBq + kAs);
-#pragma unroll
-  for (int i = 0; i < kALoads; ++i) {
-    const int idx = i * kThreads + tid;
-    const int m = (idx & 15) + 16 * (idx >> 7);
-    const int s = (idx >> 4) & (kSlots - 1);
-    aq[s * BM + m] = st.a[i];                 // [kb][h][row], s = 2*kb + h
-  }
-#pragma unroll
-  for (int i = 0; i < kBLoads; ++i) {
-    const int idx = i * kThreads + tid;
-    const int piece = idx >> 6, lane = idx & 63;
-    const int gl = piece / (2 * KBS);
-    const int kbl = (piece >> 1) % KBS;
-    const int h = piece & 1;
-    bq[(kbl * 2 + h) * BN + gl * kGroupRows + lane] = st.b[i];
-  }
-#pragma unroll
-  for (int i = 0; i < kASc; ++i) as[i * kThreads + tid] = st.as[i];   // [kb][row]
-#pragma unroll
-  for (int i = 0; i < kBSc; ++i) bs[i * kThreads + tid] = st.bs[i];   // [kb][col]
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-__global__ __launch_bounds__(kThreads, 2) void gemm_q8_mfma_kernel(
-    const int8_t* __restrict__ q_a, const uint16_t* __restrict__ d_a,
-    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws, float* __restrict__ C,
-    int64_t M, int64_t N, int64_t K, int64_t KB, int64_t NG, int64_t ldc, int tiles_m,
-    int remap) {
-  __shared__ __align__(16) uint8_t smem[2 * kStage];
+// Widen the stage's scales and store them: d_a as binary32, d_w as the pair
+// (d_w, -1.5*2^23*d_w) the epilogue consumes.
+template <class T>
+__device__ __forceinline__ void store_scales(int tid, uint8_t* buf, const uint16_t (&as_r)[T::kASc],
+                                             const uint16_t (&bs_r)[T::kBSc]) {
+  const uint32_t as = lds_addr(buf + T::kAq + T::kBq) + tid * 4;
+  const uint32_t bs = lds_addr(buf + T::kAq + T::kBq + T::kAs) + tid * 8;
+  static_for<T::kASc>([&](auto i_) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_)::value;
+    if (i * T::kThreads + tid < T::BM * T::KBS)
+      lds_write_b32<i * T::kThreads * 4>(as, f16_bits_to_f32(as_r[i]));
+  });
+  static_for<T::kBSc>([&](auto i_) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_)::value;
+    if (i * T::kThreads + tid < T::BN * T::KBS) {
+      const float w = f16_bits_to_f32(bs_r[i]);
+      lds_write_b64<i * T::kThreads * 8>(bs, v2f{w, -kBias * w});
+    }
+  });
+}
+
+// The arithmetic of one stage (KBS blocks) from an LDS buffer.  Lane-
+// dependent parts of every LDS address are in the four base registers; the
+// block, tile and row-group parts are immediate offsets.
+template <class T>
+__device__ __forceinline__ void compute_stage(uint32_t base_a, uint32_t base_as, uint32_t base_b,
+                                              uint32_t base_bs, const v16i& bias,
+                                              v16f (&acc)[T::TM][T::TN]) {
+  constexpr int TM = T::TM, TN = T::TN, BM = T::BM, BN = T::BN;
+  static_for<T::KBS>([&](auto kb_) __attribute__((always_inline)) {
+    constexpr int kb = decltype(kb_)::value;
+    v4i af[TM], avq[TM][4], bf[TN];
+    v2f wp[TN];
+    static_for<TM>([&](auto i_) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_)::value;
+      af[i] = lds_read_b128<(kb * 2 * BM + 32 * i) * 16>(base_a);
+      // Rows held by this lane in the MFMA output: 8*(r/4) + 4*half + r%4.
+      static_for<4>([&](auto q_) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_)::value;
+        avq[i][q] = lds_read_b128<(kb * BM + 32 * i + 8 * q) * 4>(base_as);
+      });
+    });
+    static_for<TN>([&](auto j_) __attribute__((always_inline)) {
+      constexpr int j = decltype(j_)::value;
+      bf[j] = lds_read_b128<(kb * 2 * BN + 32 * j) * 16>(base_b);
+      wp[j] = lds_read_b64<(kb * BN + 32 * j) * 8>(base_bs);
+    });
+    lds_wait_all();
+    static_for<TM>([&](auto i_) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_)::value;
+      after_wait(af[i]);
+      static_for<4>([&](auto q_) __attribute__((always_inline)) { after_wait(avq[i][decltype(q_)::value]); });
+    });
+    static_for<TN>([&](auto j_) __attribute__((always_inline)) {
+      after_wait(bf[decltype(j_)::value]);
+      after_wait(wp[decltype(j_)::value]);
+    });
+    // One MFMA tile at a time keeps a single 16-register partial live; the
+    // other waves of the SIMD cover the matrix-core latency.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float av[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        av[4 * q + 0] = __int_as_float(avq[i][q].x);
+        av[4 * q + 1] = __int_as_float(avq[i][q].y);
+        av[4 * q + 2] = __int_as_float(avq[i][q].z);
+        av[4 * q + 3] = __int_as_float(avq[i][q].w);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], bias, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float y = fmaf(__int_as_float(p[r]), wp[j].x, wp[j].y);
+          acc[i][j][r] = fmaf(y, av[r], acc[i][j][r]);
+        }
+      }
+    }
+    // Keep blocks apart: the block's accumulator updates complete before the
+    // next block's LDS reads are issued (otherwise the compiler hoists MFMAs
+    // of later blocks and their partials overflow the register budget).
+    static_for<TM>([&](auto i_) __attribute__((always_inline)) {
+      static_for<TN>([&](auto j_) __attribute__((always_inline)) {
+        after_wait(acc[decltype(i_)::value][decltype(j_)::value]);
+      });
+    });
+  });
+}
+
+template <class T, int kWavesPerEU>
+__global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
+void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restrict__ d_a,
+                         const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
+                         float* __restrict__ C, int64_t M, int64_t N, int64_t K, int64_t KB,
+                         int64_t NG, int64_t ldc, int tiles_m, int remap) {
+  constexpr int TM = T::TM, TN = T::TN, BM = T::BM, BN = T::BN, KBS = T::KBS;
+  __shared__ __align__(16) uint8_t smem[T::NBUF * T::kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // XCD-aware order: hardware id i lands on XCD i % 8; give each XCD a
-  // contiguous range of logical tiles.
+  // contiguous range of logical tiles (M-fastest within the range).
   int bid = blockIdx.x;
   if (remap) {
     const int per = gridDim.x >> 3;
@@ -172,83 +340,75 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_q8_mfma_kernel(
   const int64_t n0 = static_cast<int64_t>(tn) * BN;
   const int64_t g0 = n0 / kGroupRows;
 
-  const int wm0 = (wave & 1) * WM;            // wave's rows within the tile
-  const int wn0 = (wave >> 1) * WN;           // wave's columns within the tile
+  const int64_t rows_valid = (M - m0) < BM ? (M - m0) : BM;
+  const int64_t groups_valid = (NG - g0) < (BN / kGroupRows) ? (NG - g0) : (BN / kGroupRows);
+  Rsrc rs;
+  rs.ra = make_rsrc(q_a + m0 * K, static_cast<uint32_t>(rows_valid * K));
+  rs.rb = make_rsrc(wq + g0 * KB * kGroupBlockBytes,
+                    static_cast<uint32_t>(groups_valid * KB * kGroupBlockBytes));
+  rs.rsa = make_rsrc(d_a + m0 * KB, static_cast<uint32_t>(rows_valid * KB * 2));
+  rs.rsb = make_rsrc(ws + g0 * KB * kGroupRows,
+                     static_cast<uint32_t>(groups_valid * KB * kGroupRows * 2));
+  rs.KB = static_cast<int>(KB);
+  const int K32 = static_cast<int>(K);
+
+  const int wm0 = (wave % T::WAVES_M) * T::WM;
+  const int wn0 = (wave / T::WAVES_M) * T::WN;
   const int half = lane >> 5;
   const int l32 = lane & 31;
+  // lane parts of the LDS addresses read by compute_stage
+  const uint32_t lane_a = ((half * BM + wm0 + l32) * 16);
+  const uint32_t lane_as = T::kAq + T::kBq + (wm0 + 4 * half) * 4;
+  const uint32_t lane_b = T::kAq + (half * BN + wn0 + l32) * 16;
+  const uint32_t lane_bs = T::kAq + T::kBq + T::kAs + (wn0 + l32) * 8;
+  const uint32_t lds_base = lds_addr(smem);
 
-  float acc[TM][TN][16];
+  v16f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
   v16i bias;
 #pragma unroll
   for (int r = 0; r < 16; ++r) bias[r] = kBiasBits;
 
-  const int64_t nstages = (KB + KBS - 1) / KBS;
-  Staged st;
-  load_stage(st, tid, m0, g0, 0, M, K, KB, NG, q_a, d_a, wq, ws);
-  store_stage(st, tid, smem);
+  // Pipeline over NBUF stage buffers.  Iteration s: issue the quant loads
+  // of stage s+NBUF-1, compute stage s, store the scales of stage s+1
+  // (loaded during iteration s-1), load the scales of stage s+2, wait for
+  // stage s+1's quant loads, barrier.  Loads complete in issue order, so
+  // "stage s+1 has landed" is "at most kInFlight younger loads remain"; the
+  // prologue issues in the same pattern so that count holds from s = 0,
+  // and the last iterations (fewer younger loads) wait for all.
+  constexpr int NBUF = T::NBUF;
+  const int nstages = static_cast<int>((KB + KBS - 1) / KBS);
+  uint16_t as_r[T::kASc], bs_r[T::kBSc];
+  if (NBUF == 2) load_scales<T>(rs, tid, 0, as_r, bs_r);   // (NBUF > 2: loaded at t = -2)
+  for (int t = -(NBUF - 1); t < 0; ++t) {
+    if (t + NBUF - 1 < nstages)
+      issue_quants<T>(rs, wave, lane, K32, (t + NBUF - 1) * KBS,
+                      smem + ((t + NBUF - 1) % NBUF) * T::kStage);
+    if (t == -1) store_scales<T>(tid, smem, as_r, bs_r);                  // stage 0
+    if (t + 2 >= 0 && t + 2 < nstages) load_scales<T>(rs, tid, (t + 2) * KBS, as_r, bs_r);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int64_t s = 0; s < nstages; ++s) {
-    uint8_t* cur = smem + (s & 1) * kStage;
-    uint8_t* nxt = smem + ((s + 1) & 1) * kStage;
-    const bool more = s + 1 < nstages;
-    if (more) load_stage(st, tid, m0, g0, (s + 1) * KBS, M, K, KB, NG, q_a, d_a, wq, ws);
-
-    const uint4* aq = reinterpret_cast<const uint4*>(cur);
-    const uint4* bq = reinterpret_cast<const uint4*>(cur + kAq);
-    const float* as = reinterpret_cast<const float*>(cur + kAq + kBq);
-    const float* bs = reinterpret_cast<const float*>(cur + kAq + kBq + kAs);
-
-#pragma unroll 1
-    for (int kb = 0; kb < KBS; ++kb) {
-      v4i af[TM], bf[TN];
-      float av[TM][16];
-      float wv[TN], nwv[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const uint4 u = aq[(kb * 2 + half) * BM + wm0 + 32 * i + l32];
-        af[i] = v4i{static_cast<int>(u.x), static_cast<int>(u.y), static_cast<int>(u.z),
-                    static_cast<int>(u.w)};
-        // Rows held by this lane in the MFMA output: 8*(r/4) + 4*half + r%4.
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 f = *reinterpret_cast<const float4*>(
-              as + kb * BM + wm0 + 32 * i + 8 * q4 + 4 * half);
-          av[i][4 * q4 + 0] = f.x;
-          av[i][4 * q4 + 1] = f.y;
-          av[i][4 * q4 + 2] = f.z;
-          av[i][4 * q4 + 3] = f.w;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const uint4 u = bq[(kb * 2 + half) * BN + wn0 + 32 * j + l32];
-        bf[j] = v4i{static_cast<int>(u.x), static_cast<int>(u.y), static_cast<int>(u.z),
-                    static_cast<int>(u.w)};
-        wv[j] = bs[kb * BN + wn0 + 32 * j + l32];
-        nwv[j] = -kBias * wv[j];
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], bias, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float y = fmaf(__int_as_float(p[r]), wv[j], nwv[j]);
-            acc[i][j][r] = fmaf(y, av[i][r], acc[i][j][r]);
-          }
-        }
-    }
-
-    if (more) store_stage(st, tid, nxt);
+  for (int s = 0; s < nstages; ++s) {
+    const bool steady = s + NBUF - 1 < nstages && s + 2 < nstages;
+    if (s + NBUF - 1 < nstages)
+      issue_quants<T>(rs, wave, lane, K32, (s + NBUF - 1) * KBS,
+                      smem + ((s + NBUF - 1) % NBUF) * T::kStage);
+    const uint32_t b = lds_base + (s % NBUF) * T::kStage;
+    compute_stage<T>(b + lane_a, b + lane_as, b + lane_b, b + lane_bs, bias, acc);
+    if (s + 1 < nstages) store_scales<T>(tid, smem + ((s + 1) % NBUF) * T::kStage, as_r, bs_r);
+    if (s + 2 < nstages) load_scales<T>(rs, tid, (s + 2) * KBS, as_r, bs_r);
+    if (steady)
+      wait_vmcnt<T::kInFlight>();
+    else
+      wait_vmcnt<0>();
+    lds_wait_all();
     __syncthreads();
   }
 
@@ -267,21 +427,56 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_q8_mfma_kernel(
   }
 }
 
-}  // namespace
-
-hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
+template <class T, int kOcc>
+hipError_t launch_tile(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                        const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
   const int64_t KB = K / kQK;
   const int64_t NG = num_groups(N);
   const uint16_t* ws = reinterpret_cast<const uint16_t*>(w_packed + NG * KB * kGroupBlockBytes);
-  const int64_t tiles_m = (M + BM - 1) / BM;
-  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles_m = (M + T::BM - 1) / T::BM;
+  const int64_t tiles_n = (N + T::BN - 1) / T::BN;
   const int64_t grid = tiles_m * tiles_n;
   const int remap = (grid % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(gemm_q8_mfma_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
-                     stream, q_a, d_a, w_packed, ws, C, M, N, K, KB, NG, ldc,
-                     static_cast<int>(tiles_m), remap);
+  hipLaunchKernelGGL((gemm_q8_mfma_kernel<T, kOcc>), dim3(static_cast<uint32_t>(grid)),
+                     dim3(T::kThreads), 0, stream, q_a, d_a, w_packed, ws, C, M, N, K, KB, NG,
+                     ldc, static_cast<int>(tiles_m), remap);
   return hipGetLastError();
+}
+
+typedef hipError_t (*launcher_t)(int64_t, int64_t, int64_t, const int8_t*, const uint16_t*,
+                                 const uint8_t*, float*, int64_t, hipStream_t);
+
+struct TileConfig {
+  int bm, bn;
+  launcher_t launch;
+};
+
+// Compiled tile configurations.  Occupancy hint = waves per SIMD the
+// register allocation must allow.
+const TileConfig kTiles[] = {
+    {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2>, 4>},   // 0: 8 waves 32x64, KBS 4, 2 bufs
+    {128, 128, launch_tile<Tile<128, 128, 4, 2, 2, 2>, 4>},   // 1: 8 waves 32x64, KBS 2, 2 bufs
+    {64, 128, launch_tile<Tile<64, 128, 2, 2, 2, 2>, 4>},     // 2: 4 waves 32x64, KBS 2, 2 bufs
+    {128, 128, launch_tile<Tile<128, 128, 4, 2, 2, 3>, 4>},   // 3: 8 waves 32x64, KBS 2, 3 bufs
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+int pick_tile(int64_t M, int64_t N) {
+  // Q8_GEMM_TILE=<index> forces a configuration (benchmarking aid).
+  if (const char* e = getenv("Q8_GEMM_TILE")) {
+    const int t = atoi(e);
+    if (t >= 0 && t < kNumTiles) return t;
+  }
+  (void)M;
+  (void)N;
+  return 0;
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
+                       const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
+  return kTiles[pick_tile(M, N)].launch(M, N, K, q_a, d_a, w_packed, C, ldc, stream);
 }
 
 }  // namespace q8
