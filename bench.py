@@ -43,7 +43,21 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="instead of the benchmark, run device-to-device copies of MIB MiB "
+                        "(a kernel of known traffic, to scale hardware byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
 
 
 def kernel_source_sha(name):
@@ -65,6 +79,8 @@ def measured_traffic(profile_name, source, per_launch_bytes_alg):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
     if args.gpus != 1:
         sys.exit("bench.py measures one GPU: this build has no multi-GPU path "
                  "(the product shards by N or M with no communication; see DESIGN.md). "

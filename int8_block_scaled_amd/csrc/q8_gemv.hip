@@ -11,8 +11,9 @@
 // that a wave issues as one contiguous 1 KB piece, and does the int8 dots
 // on the vector ALU (v_dot4_i32_i8), not on the matrix cores.
 //
-// Work split: one workgroup per 64-row group; its waves split the K blocks
-// evenly.  Lane l of a wave owns row 64g + l.  In a piece (g, kb, h) lane l
+// Work split: one workgroup per 64-row group; its (up to 16) waves split the
+// K blocks evenly and walk their range in chunks of L blocks, all of a
+// chunk's loads in flight together.  Lane l of a wave owns row 64g + l.  In a piece (g, kb, h) lane l
 // holds bytes [16h, 16h+16) of its row's block kb, so all 64 lanes need the
 // same 16 activation bytes: those are wave-uniform and come from scalar
 // loads into SGPRs, which v_dot4 takes as its second operand.  A lane has
@@ -20,6 +21,8 @@
 // and is scaled there: acc += float(P) * (d_w * d_a), where the binary16 x
 // binary16 product is exact in binary32.  Waves then add their partial
 // sums in a fixed order through LDS, so results are reproducible.
+#include <cstdlib>
+
 #include "q8_kernels.h"
 
 namespace q8 {
@@ -28,7 +31,12 @@ namespace {
 constexpr int kMaxWaves = 16;
 constexpr int kThreads = kMaxWaves * 64;
 
-template <int MR>
+// One chunk of L blocks: all weight loads of the chunk are issued first (2 x
+// 16 bytes per lane per block, plus the binary16 scales), then the dots.
+// Block indices past the wave's range are clamped to its last block (a
+// cached re-read) and their contribution is dropped, so the code is
+// straight-line and every load of the chunk is in flight together.
+template <int MR, int L>
 __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(
     const int8_t* __restrict__ q_a, const uint16_t* __restrict__ d_a,
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
@@ -48,25 +56,35 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
 
-#pragma unroll 4
-  for (int64_t kb = kb0; kb < kb1; ++kb) {
-    const uint4 w0 = wp[(kb * 2 + 0) * 64];
-    const uint4 w1 = wp[(kb * 2 + 1) * 64];
-    const float dw = f16_bits_to_f32(sp[kb * kGroupRows]);
+  for (int64_t c = kb0; c < kb1; c += L) {
+    uint4 w0[L], w1[L];
+    float dw[L];
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const int* a = reinterpret_cast<const int*>(q_a + m * K + kb * kQK);  // wave-uniform
-      int p = 0;
-      p = __builtin_amdgcn_sdot4(static_cast<int>(w0.x), a[0], p, false);
-      p = __builtin_amdgcn_sdot4(static_cast<int>(w0.y), a[1], p, false);
-      p = __builtin_amdgcn_sdot4(static_cast<int>(w0.z), a[2], p, false);
-      p = __builtin_amdgcn_sdot4(static_cast<int>(w0.w), a[3], p, false);
-      p = __builtin_amdgcn_sdot4(static_cast<int>(w1.x), a[4], p, false);
-      p = __builtin_amdgcn_sdot4(static_cast<int>(w1.y), a[5], p, false);
-      p = __builtin_amdgcn_sdot4(static_cast<int>(w1.z), a[6], p, false);
-      p = __builtin_amdgcn_sdot4(static_cast<int>(w1.w), a[7], p, false);
-      const float s = dw * f16_bits_to_f32(d_a[m * KB + kb]);  // exact: 11 x 11 bits
-      acc[m] = fmaf(static_cast<float>(p), s, acc[m]);
+    for (int i = 0; i < L; ++i) {
+      const int64_t kb = (c + i < kb1) ? c + i : kb1 - 1;
+      w0[i] = wp[(kb * 2 + 0) * 64];
+      w1[i] = wp[(kb * 2 + 1) * 64];
+      // unconditional load (a branch here would serialise the chunk's loads)
+      dw[i] = f16_bits_to_f32(sp[kb * kGroupRows]) * (c + i < kb1 ? 1.0f : 0.0f);
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int64_t kb = (c + i < kb1) ? c + i : kb1 - 1;
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const int* a = reinterpret_cast<const int*>(q_a + m * K + kb * kQK);  // wave-uniform
+        int p = 0;
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w0[i].x), a[0], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w0[i].y), a[1], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w0[i].z), a[2], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w0[i].w), a[3], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w1[i].x), a[4], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w1[i].y), a[5], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w1[i].z), a[6], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w1[i].w), a[7], p, false);
+        const float s = dw[i] * f16_bits_to_f32(d_a[m * KB + kb]);  // exact: 11 x 11 bits
+        acc[m] = fmaf(static_cast<float>(p), s, acc[m]);
+      }
     }
   }
 
@@ -83,17 +101,32 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(
   }
 }
 
-template <int MR>
+template <int MR, int L>
 hipError_t launch_m(int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
-                    const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
+                    const uint8_t* w_packed, float* C, int64_t ldc, int max_waves,
+                    hipStream_t stream) {
   const int64_t KB = K / kQK;
   const int64_t NG = num_groups(N);
-  const int waves = static_cast<int>(KB < kMaxWaves ? KB : kMaxWaves);
+  const int waves = static_cast<int>(KB < max_waves ? KB : max_waves);
   const int kb_per_wave = static_cast<int>((KB + waves - 1) / waves);
   const uint16_t* ws = reinterpret_cast<const uint16_t*>(w_packed + NG * KB * kGroupBlockBytes);
-  hipLaunchKernelGGL(gemv_q8_kernel<MR>, dim3(static_cast<uint32_t>(NG)), dim3(waves * 64), 0,
-                     stream, q_a, d_a, w_packed, ws, C, N, K, KB, ldc, kb_per_wave);
+  hipLaunchKernelGGL((gemv_q8_kernel<MR, L>), dim3(static_cast<uint32_t>(NG)), dim3(waves * 64),
+                     0, stream, q_a, d_a, w_packed, ws, C, N, K, KB, ldc, kb_per_wave);
   return hipGetLastError();
+}
+
+template <int MR>
+hipError_t launch_cfg(int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
+                      const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
+  // Q8_GEMV_CFG=<c> (benchmarking aid): c = 0: 16 waves x chunks of 4 blocks
+  // (default), 1: 16 waves x 8, 2: 8 waves x 8.
+  int cfg = 0;
+  if (const char* e = getenv("Q8_GEMV_CFG")) cfg = atoi(e);
+  switch (cfg) {
+    case 1: return launch_m<MR, 8>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
+    case 2: return launch_m<MR, 8>(N, K, q_a, d_a, w_packed, C, ldc, 8, stream);
+    default: return launch_m<MR, 4>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
+  }
 }
 
 }  // namespace
@@ -101,14 +134,14 @@ hipError_t launch_m(int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a
 hipError_t launch_gemv(int M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                        const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
   switch (M) {
-    case 1: return launch_m<1>(N, K, q_a, d_a, w_packed, C, ldc, stream);
-    case 2: return launch_m<2>(N, K, q_a, d_a, w_packed, C, ldc, stream);
-    case 3: return launch_m<3>(N, K, q_a, d_a, w_packed, C, ldc, stream);
-    case 4: return launch_m<4>(N, K, q_a, d_a, w_packed, C, ldc, stream);
-    case 5: return launch_m<5>(N, K, q_a, d_a, w_packed, C, ldc, stream);
-    case 6: return launch_m<6>(N, K, q_a, d_a, w_packed, C, ldc, stream);
-    case 7: return launch_m<7>(N, K, q_a, d_a, w_packed, C, ldc, stream);
-    case 8: return launch_m<8>(N, K, q_a, d_a, w_packed, C, ldc, stream);
+    case 1: return launch_cfg<1>(N, K, q_a, d_a, w_packed, C, ldc, stream);
+    case 2: return launch_cfg<2>(N, K, q_a, d_a, w_packed, C, ldc, stream);
+    case 3: return launch_cfg<3>(N, K, q_a, d_a, w_packed, C, ldc, stream);
+    case 4: return launch_cfg<4>(N, K, q_a, d_a, w_packed, C, ldc, stream);
+    case 5: return launch_cfg<5>(N, K, q_a, d_a, w_packed, C, ldc, stream);
+    case 6: return launch_cfg<6>(N, K, q_a, d_a, w_packed, C, ldc, stream);
+    case 7: return launch_cfg<7>(N, K, q_a, d_a, w_packed, C, ldc, stream);
+    case 8: return launch_cfg<8>(N, K, q_a, d_a, w_packed, C, ldc, stream);
     default: return hipErrorInvalidValue;
   }
 }
