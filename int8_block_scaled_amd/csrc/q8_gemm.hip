@@ -159,33 +159,72 @@ struct Rsrc {
   int KB;
 };
 
-// Issue one stage's quant tiles: HBM -> LDS, no registers.  Per-lane
-// offsets are recomputed each stage (a few integer operations) rather than
-// held in registers across the stage's arithmetic.
+// Per-lane byte offsets of one stage's loads, relative to the stage's first
+// block (the stage adds a wave-uniform offset).  Computed once per
+// workgroup: the stage loop then spends no VALU on addressing.
 template <class T>
-__device__ __forceinline__ void issue_quants(const Rsrc& r, int wave, int lane, int K, int kb0,
-                                             uint8_t* buf) {
+struct LaneOffsets {
+  uint32_t a[T::kAInst];      // activation quant loads (into LDS)
+  uint32_t b[T::kBInst];      // weight quant loads (into LDS)
+  uint32_t sa[T::kASc];       // activation scale loads
+  uint32_t sb[T::kBSc];       // weight scale loads
+  int lim_a[T::kASc];         // the scale load is in range while kb0 < lim
+  int lim_b[T::kBSc];
+};
+
+template <class T>
+__device__ __forceinline__ void lane_offsets(LaneOffsets<T>& o, int tid, int wave, int lane,
+                                             uint32_t K, uint32_t KB) {
+  constexpr uint32_t BM = T::BM, BN = T::BN, KBS = T::KBS;
+#pragma unroll
+  for (int u0 = 0; u0 < T::kAInst; ++u0) {
+    const uint32_t u = wave * T::kAInst + u0;
+    const uint32_t s = u / (BM / 64), mb = u % (BM / 64);
+    o.a[u0] = (mb * 64 + lane) * K + s * 16;
+  }
+#pragma unroll
+  for (int u0 = 0; u0 < T::kBInst; ++u0) {
+    const uint32_t u = wave * T::kBInst + u0;
+    const uint32_t gl = u / (2 * KBS), kbl = (u >> 1) % KBS, h = u & 1;
+    o.b[u0] = ((gl * KB + kbl) * 2 + h) * kPieceBytes + lane * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < T::kASc; ++i) {
+    const uint32_t idx = i * T::kThreads + tid;
+    const uint32_t m = idx % BM, kbl = idx / BM;
+    o.sa[i] = (m * KB + kbl) * 2;
+    o.lim_a[i] = idx < BM * KBS ? static_cast<int>(KB - kbl) : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < T::kBSc; ++i) {
+    const uint32_t idx = i * T::kThreads + tid;
+    const uint32_t n = idx % BN, kbl = idx / BN;
+    o.sb[i] = (((n / kGroupRows) * KB + kbl) * kGroupRows + n % kGroupRows) * 2;
+    o.lim_b[i] = idx < BN * KBS ? static_cast<int>(KB - kbl) : 0;
+  }
+}
+
+// Issue one stage's quant tiles: HBM -> LDS, no registers.
+template <class T>
+__device__ __forceinline__ void issue_quants(const Rsrc& r, const LaneOffsets<T>& o, int wave,
+                                             int kb0, uint8_t* buf) {
 #if __HIP_DEVICE_COMPILE__   // the buffer builtins exist only in the device pass
   constexpr int BM = T::BM, BN = T::BN, KBS = T::KBS;
   kb0 = __builtin_amdgcn_readfirstlane(kb0);   // wave-uniform: the loads' scalar offsets
-  asm volatile("" : "+v"(lane));               // opaque: do not hoist the offsets below
 #pragma unroll
   for (int u0 = 0; u0 < T::kAInst; ++u0) {
     const int u = wave * T::kAInst + u0;
     const int s = u / (BM / 64), mb = u % (BM / 64);
-    const uint32_t voff = static_cast<uint32_t>((mb * 64 + lane) * K + s * 16);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ra, (lds_void_ptr)(buf + (s * BM + mb * 64) * 16),
-                                             16, voff, static_cast<uint32_t>(kb0 * kQK), 0, 0);
+                                             16, o.a[u0], static_cast<uint32_t>(kb0 * kQK), 0, 0);
   }
 #pragma unroll
   for (int u0 = 0; u0 < T::kBInst; ++u0) {
     const int u = wave * T::kBInst + u0;
     const int gl = u / (2 * KBS), kbl = (u >> 1) % KBS, h = u & 1;
-    const uint32_t voff =
-        static_cast<uint32_t>(((gl * r.KB + kbl) * 2 + h) * kPieceBytes + lane * 16);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r.rb, (lds_void_ptr)(buf + T::kAq + ((kbl * 2 + h) * BN + gl * kGroupRows) * 16), 16,
-        voff, static_cast<uint32_t>(kb0 * kGroupBlockBytes), 0, 0);
+        o.b[u0], static_cast<uint32_t>(kb0 * kGroupBlockBytes), 0, 0);
   }
 #endif
 }
@@ -193,31 +232,18 @@ __device__ __forceinline__ void issue_quants(const Rsrc& r, int wave, int lane, 
 // Load one stage's binary16 scales into registers (blocks past K/32 read as
 // zero through an out-of-range offset).
 template <class T>
-__device__ __forceinline__ void load_scales(const Rsrc& r, int tid, int kb0,
+__device__ __forceinline__ void load_scales(const Rsrc& r, const LaneOffsets<T>& o, int kb0,
                                             uint16_t (&as_r)[T::kASc], uint16_t (&bs_r)[T::kBSc]) {
 #if __HIP_DEVICE_COMPILE__
-  constexpr int BM = T::BM, BN = T::BN, KBS = T::KBS;
   kb0 = __builtin_amdgcn_readfirstlane(kb0);
-  asm volatile("" : "+v"(tid));
 #pragma unroll
-  for (int i = 0; i < T::kASc; ++i) {
-    const int idx = i * T::kThreads + tid;
-    const int m = idx % BM, kbl = idx / BM;
-    const bool in = idx < BM * KBS && kb0 + kbl < r.KB;
-    const uint32_t off = in ? static_cast<uint32_t>((m * r.KB + kbl) * 2) : kOutOfRange;
-    as_r[i] = __builtin_amdgcn_raw_buffer_load_b16(r.rsa, off, static_cast<uint32_t>(kb0 * 2), 0);
-  }
+  for (int i = 0; i < T::kASc; ++i)
+    as_r[i] = __builtin_amdgcn_raw_buffer_load_b16(r.rsa, kb0 < o.lim_a[i] ? o.sa[i] : kOutOfRange,
+                                                   static_cast<uint32_t>(kb0 * 2), 0);
 #pragma unroll
-  for (int i = 0; i < T::kBSc; ++i) {
-    const int idx = i * T::kThreads + tid;
-    const int n = idx % BN, kbl = idx / BN;
-    const bool in = idx < BN * KBS && kb0 + kbl < r.KB;
-    const uint32_t off =
-        in ? static_cast<uint32_t>((((n / kGroupRows) * r.KB + kbl) * kGroupRows + n % kGroupRows) * 2)
-           : kOutOfRange;
-    bs_r[i] = __builtin_amdgcn_raw_buffer_load_b16(r.rsb, off,
+  for (int i = 0; i < T::kBSc; ++i)
+    bs_r[i] = __builtin_amdgcn_raw_buffer_load_b16(r.rsb, kb0 < o.lim_b[i] ? o.sb[i] : kOutOfRange,
                                                    static_cast<uint32_t>(kb0 * kGroupRows * 2), 0);
-  }
 #endif
 }
 
@@ -350,7 +376,8 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   rs.rsb = make_rsrc(ws + g0 * KB * kGroupRows,
                      static_cast<uint32_t>(groups_valid * KB * kGroupRows * 2));
   rs.KB = static_cast<int>(KB);
-  const int K32 = static_cast<int>(K);
+  LaneOffsets<T> lo;
+  lane_offsets<T>(lo, tid, wave, lane, static_cast<uint32_t>(K), static_cast<uint32_t>(KB));
 
   const int wm0 = (wave % T::WAVES_M) * T::WM;
   const int wn0 = (wave / T::WAVES_M) * T::WN;
@@ -384,13 +411,13 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   constexpr int NBUF = T::NBUF;
   const int nstages = static_cast<int>((KB + KBS - 1) / KBS);
   uint16_t as_r[T::kASc], bs_r[T::kBSc];
-  if (NBUF == 2) load_scales<T>(rs, tid, 0, as_r, bs_r);   // (NBUF > 2: loaded at t = -2)
+  if (NBUF == 2) load_scales<T>(rs, lo, 0, as_r, bs_r);   // (NBUF > 2: loaded at t = -2)
   for (int t = -(NBUF - 1); t < 0; ++t) {
     if (t + NBUF - 1 < nstages)
-      issue_quants<T>(rs, wave, lane, K32, (t + NBUF - 1) * KBS,
+      issue_quants<T>(rs, lo, wave, (t + NBUF - 1) * KBS,
                       smem + ((t + NBUF - 1) % NBUF) * T::kStage);
     if (t == -1) store_scales<T>(tid, smem, as_r, bs_r);                  // stage 0
-    if (t + 2 >= 0 && t + 2 < nstages) load_scales<T>(rs, tid, (t + 2) * KBS, as_r, bs_r);
+    if (t + 2 >= 0 && t + 2 < nstages) load_scales<T>(rs, lo, (t + 2) * KBS, as_r, bs_r);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -398,12 +425,12 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   for (int s = 0; s < nstages; ++s) {
     const bool steady = s + NBUF - 1 < nstages && s + 2 < nstages;
     if (s + NBUF - 1 < nstages)
-      issue_quants<T>(rs, wave, lane, K32, (s + NBUF - 1) * KBS,
+      issue_quants<T>(rs, lo, wave, (s + NBUF - 1) * KBS,
                       smem + ((s + NBUF - 1) % NBUF) * T::kStage);
     const uint32_t b = lds_base + (s % NBUF) * T::kStage;
     compute_stage<T>(b + lane_a, b + lane_as, b + lane_b, b + lane_bs, bias, acc);
     if (s + 1 < nstages) store_scales<T>(tid, smem + ((s + 1) % NBUF) * T::kStage, as_r, bs_r);
-    if (s + 2 < nstages) load_scales<T>(rs, tid, (s + 2) * KBS, as_r, bs_r);
+    if (s + 2 < nstages) load_scales<T>(rs, lo, (s + 2) * KBS, as_r, bs_r);
     if (steady)
       wait_vmcnt<T::kInFlight>();
     else
