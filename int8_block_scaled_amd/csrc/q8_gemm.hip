@@ -62,7 +62,7 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr float kBias = 12582912.0f;            // 1.5 * 2^23
 constexpr int kBiasBits = 0x4B400000;           // its binary32 bits
-constexpr uint32_t kOutOfRange = 0xFFFFFFFFu;   // buffer offset that reads as zero
+[[maybe_unused]] constexpr uint32_t kOutOfRange = 0xFFFFFFFFu;   // buffer offset that reads as zero
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int KBS_, int NBUF_>
 struct Tile {
@@ -156,6 +156,7 @@ struct Rsrc {
   __amdgpu_buffer_rsrc_t rb;    // packed quant pieces of the tile's row groups
   __amdgpu_buffer_rsrc_t rsa;   // d_a rows [m0, m0 + rows_valid)
   __amdgpu_buffer_rsrc_t rsb;   // weight scales of the tile's row groups
+  __amdgpu_buffer_rsrc_t rnull; // empty range: every load reads zero, touches no memory
   int KB;
 };
 
@@ -211,11 +212,16 @@ __device__ __forceinline__ void issue_quants(const Rsrc& r, const LaneOffsets<T>
 #if __HIP_DEVICE_COMPILE__   // the buffer builtins exist only in the device pass
   constexpr int BM = T::BM, BN = T::BN, KBS = T::KBS;
   kb0 = __builtin_amdgcn_readfirstlane(kb0);   // wave-uniform: the loads' scalar offsets
+  // Stages past the end load nothing (the pipeline issues them anyway so
+  // that its wait counts are the same every iteration).
+  const bool live = kb0 < r.KB;
+  const __amdgpu_buffer_rsrc_t ra = live ? r.ra : r.rnull;
+  const __amdgpu_buffer_rsrc_t rb = live ? r.rb : r.rnull;
 #pragma unroll
   for (int u0 = 0; u0 < T::kAInst; ++u0) {
     const int u = wave * T::kAInst + u0;
     const int s = u / (BM / 64), mb = u % (BM / 64);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.ra, (lds_void_ptr)(buf + (s * BM + mb * 64) * 16),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_ptr)(buf + (s * BM + mb * 64) * 16),
                                              16, o.a[u0], static_cast<uint32_t>(kb0 * kQK), 0, 0);
   }
 #pragma unroll
@@ -223,7 +229,7 @@ __device__ __forceinline__ void issue_quants(const Rsrc& r, const LaneOffsets<T>
     const int u = wave * T::kBInst + u0;
     const int gl = u / (2 * KBS), kbl = (u >> 1) % KBS, h = u & 1;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r.rb, (lds_void_ptr)(buf + T::kAq + ((kbl * 2 + h) * BN + gl * kGroupRows) * 16), 16,
+        rb, (lds_void_ptr)(buf + T::kAq + ((kbl * 2 + h) * BN + gl * kGroupRows) * 16), 16,
         o.b[u0], static_cast<uint32_t>(kb0 * kGroupBlockBytes), 0, 0);
   }
 #endif
@@ -375,6 +381,7 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   rs.rsa = make_rsrc(d_a + m0 * KB, static_cast<uint32_t>(rows_valid * KB * 2));
   rs.rsb = make_rsrc(ws + g0 * KB * kGroupRows,
                      static_cast<uint32_t>(groups_valid * KB * kGroupRows * 2));
+  rs.rnull = make_rsrc(q_a, 0);
   rs.KB = static_cast<int>(KB);
   LaneOffsets<T> lo;
   lane_offsets<T>(lo, tid, wave, lane, static_cast<uint32_t>(K), static_cast<uint32_t>(KB));
@@ -403,41 +410,39 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
 
   // Pipeline over NBUF stage buffers.  Iteration s: issue the quant loads
   // of stage s+NBUF-1, compute stage s, store the scales of stage s+1
-  // (loaded during iteration s-1), load the scales of stage s+2, wait for
-  // stage s+1's quant loads, barrier.  Loads complete in issue order, so
-  // "stage s+1 has landed" is "at most kInFlight younger loads remain"; the
-  // prologue issues in the same pattern so that count holds from s = 0,
-  // and the last iterations (fewer younger loads) wait for all.
+  // (loaded one iteration earlier), load the scales of stage s+2, wait for
+  // stage s+1's quant loads, barrier.  Every iteration issues the same
+  // loads (stages past the end read zeros and touch no memory) so that
+  // "stage s+1 has landed" is always "at most kInFlight younger loads
+  // remain": loads complete in issue order.
   constexpr int NBUF = T::NBUF;
   const int nstages = static_cast<int>((KB + KBS - 1) / KBS);
   uint16_t as_r[T::kASc], bs_r[T::kBSc];
   if (NBUF == 2) load_scales<T>(rs, lo, 0, as_r, bs_r);   // (NBUF > 2: loaded at t = -2)
   for (int t = -(NBUF - 1); t < 0; ++t) {
-    if (t + NBUF - 1 < nstages)
-      issue_quants<T>(rs, lo, wave, (t + NBUF - 1) * KBS,
-                      smem + ((t + NBUF - 1) % NBUF) * T::kStage);
+    issue_quants<T>(rs, lo, wave, (t + NBUF - 1) * KBS, smem + ((t + NBUF - 1) % NBUF) * T::kStage);
     if (t == -1) store_scales<T>(tid, smem, as_r, bs_r);                  // stage 0
-    if (t + 2 >= 0 && t + 2 < nstages) load_scales<T>(rs, lo, (t + 2) * KBS, as_r, bs_r);
+    if (t + 2 >= 0) load_scales<T>(rs, lo, (t + 2) * KBS, as_r, bs_r);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int s = 0; s < nstages; ++s) {
-    const bool steady = s + NBUF - 1 < nstages && s + 2 < nstages;
-    if (s + NBUF - 1 < nstages)
-      issue_quants<T>(rs, lo, wave, (s + NBUF - 1) * KBS,
-                      smem + ((s + NBUF - 1) % NBUF) * T::kStage);
+    issue_quants<T>(rs, lo, wave, (s + NBUF - 1) * KBS,
+                    smem + ((s + NBUF - 1) % NBUF) * T::kStage);
     const uint32_t b = lds_base + (s % NBUF) * T::kStage;
     compute_stage<T>(b + lane_a, b + lane_as, b + lane_b, b + lane_bs, bias, acc);
-    if (s + 1 < nstages) store_scales<T>(tid, smem + ((s + 1) % NBUF) * T::kStage, as_r, bs_r);
-    if (s + 2 < nstages) load_scales<T>(rs, lo, (s + 2) * KBS, as_r, bs_r);
-    if (steady)
-      wait_vmcnt<T::kInFlight>();
-    else
-      wait_vmcnt<0>();
+    store_scales<T>(tid, smem + ((s + 1) % NBUF) * T::kStage, as_r, bs_r);
+    load_scales<T>(rs, lo, (s + 2) * KBS, as_r, bs_r);
+    wait_vmcnt<T::kInFlight>();
     lds_wait_all();
-    __syncthreads();
+    // A bare barrier: __syncthreads() would add a release fence, for which
+    // the compiler waits on every outstanding load (the direct-to-LDS loads
+    // count as LDS writes), draining the loads issued for later stages.
+    // The waits above already cover what the next stage reads.
+    asm volatile("s_barrier" ::: "memory");
   }
+  wait_vmcnt<0>();   // the loads issued past the end are done before LDS is released
 
   // Output: lane holds column wn0 + 32j + l32 and rows 8*(r/4) + 4*half + r%4.
 #pragma unroll
