@@ -47,6 +47,7 @@
 // each of the 8 XCDs (which receive workgroups round-robin) gets one
 // contiguous range of tiles and keeps its weight tiles in its own L2.
 #include <cstdlib>
+#include <type_traits>
 #include <utility>
 
 #include "q8_kernels.h"
@@ -54,9 +55,11 @@
 namespace q8 {
 namespace {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
@@ -64,14 +67,18 @@ constexpr float kBias = 12582912.0f;            // 1.5 * 2^23
 constexpr int kBiasBits = 0x4B400000;           // its binary32 bits
 [[maybe_unused]] constexpr uint32_t kOutOfRange = 0xFFFFFFFFu;   // buffer offset that reads as zero
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int KBS_, int NBUF_>
+// MF: output tile of one MFMA, 32 (v_mfma_i32_32x32x32_i8) or 16
+// (v_mfma_i32_16x16x32_i8).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int KBS_, int NBUF_, int MF_ = 32>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, KBS = KBS_;
   static constexpr int NBUF = NBUF_;                           // LDS stage buffers
+  static constexpr int MF = MF_;
+  static constexpr int kAccN = MF * MF / 64;                   // accumulator values per lane and tile
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // per-wave tile
-  static constexpr int TM = WM / 32, TN = WN / 32;             // MFMA tiles per wave
+  static constexpr int TM = WM / MF, TN = WN / MF;             // MFMA tiles per wave
   static constexpr int kSlots = 2 * KBS;                       // 16-byte slots per row per stage
   // LDS per stage (bytes)
   static constexpr int kAq = KBS * 2 * BM * 16;                // activation quants [kb][h][row]
@@ -84,7 +91,8 @@ struct Tile {
   static constexpr int kBInst = (BN / kGroupRows) * 2 * KBS / kWaves;
   static constexpr int kASc = (BM * KBS + kThreads - 1) / kThreads;
   static constexpr int kBSc = (BN * KBS + kThreads - 1) / kThreads;
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(MF == 32 || MF == 16, "MFMA shape");
+  static_assert(WM % MF == 0 && WN % MF == 0, "wave tile must be a multiple of the MFMA tile");
   static_assert(BN % kGroupRows == 0, "BN must cover whole 64-row groups");
   static_assert(BM % 64 == 0, "activation loads cover 64 rows each");
   static_assert(kAInst * 64 * kWaves == BM * kSlots, "activation loads split over waves");
@@ -205,32 +213,38 @@ __device__ __forceinline__ void lane_offsets(LaneOffsets<T>& o, int tid, int wav
   }
 }
 
-// Issue one stage's quant tiles: HBM -> LDS, no registers.
-template <class T>
+// Issue quant loads [P0, P1) of one stage (the wave's activation loads,
+// then its weight loads): HBM -> LDS, no registers.  The stage loop spreads
+// a stage's loads over the blocks of the previous stage's arithmetic, so a
+// wave never queues all of them at once behind the other waves' loads.
+template <class T, int P0, int P1>
 __device__ __forceinline__ void issue_quants(const Rsrc& r, const LaneOffsets<T>& o, int wave,
                                              int kb0, uint8_t* buf) {
 #if __HIP_DEVICE_COMPILE__   // the buffer builtins exist only in the device pass
   constexpr int BM = T::BM, BN = T::BN, KBS = T::KBS;
-  kb0 = __builtin_amdgcn_readfirstlane(kb0);   // wave-uniform: the loads' scalar offsets
-  // Stages past the end load nothing (the pipeline issues them anyway so
-  // that its wait counts are the same every iteration).
-  const bool live = kb0 < r.KB;
-  const __amdgpu_buffer_rsrc_t ra = live ? r.ra : r.rnull;
-  const __amdgpu_buffer_rsrc_t rb = live ? r.rb : r.rnull;
-#pragma unroll
-  for (int u0 = 0; u0 < T::kAInst; ++u0) {
-    const int u = wave * T::kAInst + u0;
-    const int s = u / (BM / 64), mb = u % (BM / 64);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_ptr)(buf + (s * BM + mb * 64) * 16),
-                                             16, o.a[u0], static_cast<uint32_t>(kb0 * kQK), 0, 0);
-  }
-#pragma unroll
-  for (int u0 = 0; u0 < T::kBInst; ++u0) {
-    const int u = wave * T::kBInst + u0;
-    const int gl = u / (2 * KBS), kbl = (u >> 1) % KBS, h = u & 1;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (lds_void_ptr)(buf + T::kAq + ((kbl * 2 + h) * BN + gl * kGroupRows) * 16), 16,
-        o.b[u0], static_cast<uint32_t>(kb0 * kGroupBlockBytes), 0, 0);
+  if constexpr (P0 < P1) {
+    kb0 = __builtin_amdgcn_readfirstlane(kb0);   // wave-uniform: the loads' scalar offsets
+    // Stages past the end load nothing (the pipeline issues them anyway so
+    // that its wait counts are the same every iteration).
+    const bool live = kb0 < r.KB;
+    const __amdgpu_buffer_rsrc_t ra = live ? r.ra : r.rnull;
+    const __amdgpu_buffer_rsrc_t rb = live ? r.rb : r.rnull;
+    static_for<P1 - P0>([&](auto p_) __attribute__((always_inline)) {
+      constexpr int pi = P0 + decltype(p_)::value;
+      if constexpr (pi < T::kAInst) {
+        const int u = wave * T::kAInst + pi;
+        const int s = u / (BM / 64), mb = u % (BM / 64);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_ptr)(buf + (s * BM + mb * 64) * 16),
+                                                 16, o.a[pi], static_cast<uint32_t>(kb0 * kQK), 0, 0);
+      } else {
+        constexpr int u0 = pi - T::kAInst;
+        const int u = wave * T::kBInst + u0;
+        const int gl = u / (2 * KBS), kbl = (u >> 1) % KBS, h = u & 1;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (lds_void_ptr)(buf + T::kAq + ((kbl * 2 + h) * BN + gl * kGroupRows) * 16), 16,
+            o.b[u0], static_cast<uint32_t>(kb0 * kGroupBlockBytes), 0, 0);
+      }
+    });
   }
 #endif
 }
@@ -282,10 +296,10 @@ __device__ __forceinline__ void store_scales(int tid, uint8_t* buf, const uint16
 // The arithmetic of one stage (KBS blocks) from an LDS buffer.  Lane-
 // dependent parts of every LDS address are in the four base registers; the
 // block, tile and row-group parts are immediate offsets.
-template <class T>
+template <class T, class F>
 __device__ __forceinline__ void compute_stage(uint32_t base_a, uint32_t base_as, uint32_t base_b,
                                               uint32_t base_bs, const v16i& bias,
-                                              v16f (&acc)[T::TM][T::TN]) {
+                                              v16f (&acc)[T::TM][T::TN], F&& at_block) {
   constexpr int TM = T::TM, TN = T::TN, BM = T::BM, BN = T::BN;
   static_for<T::KBS>([&](auto kb_) __attribute__((always_inline)) {
     constexpr int kb = decltype(kb_)::value;
@@ -305,6 +319,7 @@ __device__ __forceinline__ void compute_stage(uint32_t base_a, uint32_t base_as,
       bf[j] = lds_read_b128<(kb * 2 * BN + 32 * j) * 16>(base_b);
       wp[j] = lds_read_b64<(kb * BN + 32 * j) * 8>(base_bs);
     });
+    at_block(kb_);
     lds_wait_all();
     static_for<TM>([&](auto i_) __attribute__((always_inline)) {
       constexpr int i = decltype(i_)::value;
@@ -345,6 +360,93 @@ __device__ __forceinline__ void compute_stage(uint32_t base_a, uint32_t base_as,
         after_wait(acc[decltype(i_)::value][decltype(j_)::value]);
       });
     });
+  });
+}
+
+// Operands of one block for a wave's 16x16 tiles: quant fragments (lane l:
+// row or column l%16, block bytes 8*(l/16) .. +8), d_a for the lane's four
+// output rows of each row tile, and the (d_w, -1.5*2^23*d_w) pair of the
+// lane's column of each column tile.
+template <class T>
+struct Frag16 {
+  v2i a[T::TM], b[T::TN];
+  v4f as[T::TM];
+  v2f ws[T::TN];
+};
+
+template <class T, int KB>
+__device__ __forceinline__ void read_frag16(Frag16<T>& f, uint32_t base_a, uint32_t base_as,
+                                            uint32_t base_b, uint32_t base_bs) {
+  constexpr int BM = T::BM, BN = T::BN;
+  static_for<T::TM>([&](auto i_) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_)::value;
+    const v2f a = lds_read_b64<(KB * 2 * BM + 16 * i) * 16>(base_a);
+    f.a[i] = __builtin_bit_cast(v2i, a);
+    const v4i s = lds_read_b128<(KB * BM + 16 * i) * 4>(base_as);
+    f.as[i] = __builtin_bit_cast(v4f, s);
+  });
+  static_for<T::TN>([&](auto j_) __attribute__((always_inline)) {
+    constexpr int j = decltype(j_)::value;
+    const v2f b = lds_read_b64<(KB * 2 * BN + 16 * j) * 16>(base_b);
+    f.b[j] = __builtin_bit_cast(v2i, b);
+    f.ws[j] = lds_read_b64<(KB * BN + 16 * j) * 8>(base_bs);
+  });
+}
+
+template <class T>
+__device__ __forceinline__ void tie_frag16(Frag16<T>& f) {
+  static_for<T::TM>([&](auto i_) __attribute__((always_inline)) {
+    after_wait(f.a[decltype(i_)::value]);
+    after_wait(f.as[decltype(i_)::value]);
+  });
+  static_for<T::TN>([&](auto j_) __attribute__((always_inline)) {
+    after_wait(f.b[decltype(j_)::value]);
+    after_wait(f.ws[decltype(j_)::value]);
+  });
+}
+
+// One stage with 16x16 MFMAs, software-pipelined inside the wave: the MFMA
+// of tile u+1 is issued before the epilogue of tile u (so its latency is
+// covered by this wave's own FMAs), and the operands of block kb+1 are read
+// from LDS while block kb is computed.  The empty asm statements order the
+// schedule: the MFMA of tile u+2 takes the bias register as it stands after
+// the epilogue of tile u, so at most two partials are live.
+template <class T, class F>
+__device__ __forceinline__ void compute_stage16(uint32_t base_a, uint32_t base_as, uint32_t base_b,
+                                                uint32_t base_bs, v4i& bias,
+                                                v4f (&acc)[T::TM][T::TN], F&& at_block) {
+  constexpr int TM = T::TM, TN = T::TN, NT = TM * TN, KBS = T::KBS;
+  Frag16<T> f[2];
+  read_frag16<T, 0>(f[0], base_a, base_as, base_b, base_bs);
+  lds_wait_all();
+  tie_frag16<T>(f[0]);
+  v4i p[2];
+  p[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+      __builtin_bit_cast(long, f[0].a[0]), __builtin_bit_cast(long, f[0].b[0]), bias, 0, 0, 0);
+  static_for<KBS * NT>([&](auto u_) __attribute__((always_inline)) {
+    constexpr int u = decltype(u_)::value;
+    constexpr int kb = u / NT, t = u % NT, i = t / TN, j = t % TN;
+    Frag16<T>& cur = f[kb & 1];
+    if constexpr (t == 0 && kb + 1 < KBS)
+      read_frag16<T, kb + 1>(f[(kb + 1) & 1], base_a, base_as, base_b, base_bs);
+    if constexpr (t == 0) at_block(std::integral_constant<int, kb>{});
+    if constexpr (u + 1 < KBS * NT) {
+      constexpr int kb1 = (u + 1) / NT, t1 = (u + 1) % NT, i1 = t1 / TN, j1 = t1 % TN;
+      if constexpr (t1 == 0) {   // first tile of the next block: its operands must be in
+        lds_wait_all();
+        tie_frag16<T>(f[kb1 & 1]);
+      }
+      Frag16<T>& nxt = f[kb1 & 1];
+      p[(u + 1) & 1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+          __builtin_bit_cast(long, nxt.a[i1]), __builtin_bit_cast(long, nxt.b[j1]), bias, 0, 0, 0);
+    }
+    const v4i& pu = p[u & 1];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float y = fmaf(__int_as_float(pu[r]), cur.ws[j].x, cur.ws[j].y);
+      acc[i][j][r] = fmaf(y, cur.as[i][r], acc[i][j][r]);
+    }
+    asm volatile("" : "+v"(acc[i][j]), "+v"(bias));
   });
 }
 
@@ -391,25 +493,32 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   const int half = lane >> 5;
   const int l32 = lane & 31;
   // lane parts of the LDS addresses read by compute_stage
-  const uint32_t lane_a = ((half * BM + wm0 + l32) * 16);
-  const uint32_t lane_as = T::kAq + T::kBq + (wm0 + 4 * half) * 4;
-  const uint32_t lane_b = T::kAq + (half * BN + wn0 + l32) * 16;
-  const uint32_t lane_bs = T::kAq + T::kBq + T::kAs + (wn0 + l32) * 8;
+  // (32x32: lane l reads row/column l%32, half l/32; 16x16: row/column
+  // l%16, bytes 8*(l/16) .. +8 of the block, i.e. half g/2, offset 8*(g%2))
+  const int g = lane >> 4, l16 = lane & 15;
+  const uint32_t lane_a = T::MF == 32 ? (half * BM + wm0 + l32) * 16
+                                      : ((g >> 1) * BM + wm0 + l16) * 16 + (g & 1) * 8;
+  const uint32_t lane_as = T::kAq + T::kBq + (wm0 + (T::MF == 32 ? 4 * half : 4 * g)) * 4;
+  const uint32_t lane_b = T::MF == 32 ? T::kAq + (half * BN + wn0 + l32) * 16
+                                      : T::kAq + ((g >> 1) * BN + wn0 + l16) * 16 + (g & 1) * 8;
+  const uint32_t lane_bs = T::kAq + T::kBq + T::kAs + (wn0 + (T::MF == 32 ? l32 : l16)) * 8;
   const uint32_t lds_base = lds_addr(smem);
 
-  v16f acc[TM][TN];
+  using acc_t = std::conditional_t<T::MF == 32, v16f, v4f>;
+  using bias_t = std::conditional_t<T::MF == 32, v16i, v4i>;
+  acc_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  v16i bias;
+      for (int r = 0; r < T::kAccN; ++r) acc[i][j][r] = 0.0f;
+  bias_t bias;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) bias[r] = kBiasBits;
+  for (int r = 0; r < T::kAccN; ++r) bias[r] = kBiasBits;
 
-  // Pipeline over NBUF stage buffers.  Iteration s: issue the quant loads
-  // of stage s+NBUF-1, compute stage s, store the scales of stage s+1
+  // Pipeline over NBUF stage buffers.  Iteration s: compute stage s while
+  // issuing the quant loads of stage s+NBUF-1, store the scales of stage s+1
   // (loaded one iteration earlier), load the scales of stage s+2, wait for
   // stage s+1's quant loads, barrier.  Every iteration issues the same
   // loads (stages past the end read zeros and touch no memory) so that
@@ -420,7 +529,8 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   uint16_t as_r[T::kASc], bs_r[T::kBSc];
   if (NBUF == 2) load_scales<T>(rs, lo, 0, as_r, bs_r);   // (NBUF > 2: loaded at t = -2)
   for (int t = -(NBUF - 1); t < 0; ++t) {
-    issue_quants<T>(rs, lo, wave, (t + NBUF - 1) * KBS, smem + ((t + NBUF - 1) % NBUF) * T::kStage);
+    issue_quants<T, 0, T::kDmaOps>(rs, lo, wave, (t + NBUF - 1) * KBS,
+                                   smem + ((t + NBUF - 1) % NBUF) * T::kStage);
     if (t == -1) store_scales<T>(tid, smem, as_r, bs_r);                  // stage 0
     if (t + 2 >= 0) load_scales<T>(rs, lo, (t + 2) * KBS, as_r, bs_r);
   }
@@ -428,10 +538,19 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   __syncthreads();
 
   for (int s = 0; s < nstages; ++s) {
-    issue_quants<T>(rs, lo, wave, (s + NBUF - 1) * KBS,
-                    smem + ((s + NBUF - 1) % NBUF) * T::kStage);
+    // this stage's share of the loads of stage s+NBUF-1, issued block by block
+    uint8_t* const next = smem + ((s + NBUF - 1) % NBUF) * T::kStage;
+    const int kb_next = (s + NBUF - 1) * KBS;
+    auto at_block = [&](auto kb_) __attribute__((always_inline)) {
+      constexpr int kb = decltype(kb_)::value;
+      issue_quants<T, kb * T::kDmaOps / KBS, (kb + 1) * T::kDmaOps / KBS>(rs, lo, wave, kb_next,
+                                                                           next);
+    };
     const uint32_t b = lds_base + (s % NBUF) * T::kStage;
-    compute_stage<T>(b + lane_a, b + lane_as, b + lane_b, b + lane_bs, bias, acc);
+    if constexpr (T::MF == 32)
+      compute_stage<T>(b + lane_a, b + lane_as, b + lane_b, b + lane_bs, bias, acc, at_block);
+    else
+      compute_stage16<T>(b + lane_a, b + lane_as, b + lane_b, b + lane_bs, bias, acc, at_block);
     store_scales<T>(tid, smem + ((s + 1) % NBUF) * T::kStage, as_r, bs_r);
     load_scales<T>(rs, lo, (s + 2) * KBS, as_r, bs_r);
     wait_vmcnt<T::kInFlight>();
@@ -444,16 +563,18 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   }
   wait_vmcnt<0>();   // the loads issued past the end are done before LDS is released
 
-  // Output: lane holds column wn0 + 32j + l32 and rows 8*(r/4) + 4*half + r%4.
+  // Output.  32x32: lane holds column wn0 + 32j + l32 and rows
+  // 8*(r/4) + 4*half + r%4; 16x16: column wn0 + 16j + l16, rows 4*g + r.
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int64_t col = n0 + wn0 + 32 * j + l32;
+    const int64_t col = n0 + wn0 + T::MF * j + (T::MF == 32 ? l32 : l16);
     if (col >= N) continue;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+      for (int r = 0; r < T::kAccN; ++r) {
+        const int64_t row = m0 + wm0 + T::MF * i +
+                            (T::MF == 32 ? 8 * (r >> 2) + 4 * half + (r & 3) : 4 * g + r);
         if (row < M) C[row * ldc + col] = acc[i][j][r];
       }
   }
@@ -490,6 +611,9 @@ const TileConfig kTiles[] = {
     {128, 128, launch_tile<Tile<128, 128, 4, 2, 2, 2>, 4>},   // 1: 8 waves 32x64, KBS 2, 2 bufs
     {64, 128, launch_tile<Tile<64, 128, 2, 2, 2, 2>, 4>},     // 2: 4 waves 32x64, KBS 2, 2 bufs
     {128, 128, launch_tile<Tile<128, 128, 4, 2, 2, 3>, 4>},   // 3: 8 waves 32x64, KBS 2, 3 bufs
+    {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2, 16>, 4>},   // 4: as 0 on 16x16 MFMAs
+    {128, 128, launch_tile<Tile<128, 128, 4, 2, 2, 2, 16>, 4>},   // 5: as 1 on 16x16 MFMAs
+    {64, 128, launch_tile<Tile<64, 128, 2, 2, 2, 2, 16>, 4>},     // 6: as 2 on 16x16 MFMAs
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
