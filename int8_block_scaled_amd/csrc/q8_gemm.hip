@@ -8,7 +8,9 @@
 // the list of non-throttled paths).  MI355X has full-rate int8 matrix
 // cores, so here the block dots run on v_mfma_i32_32x32x32_i8, whose K of
 // 32 is exactly one Q8_0 block: one instruction gives the exact int32 dot
-// of one block for a 32x32 output tile.
+// of one block for a 32x32 output tile.  A variant runs on
+// v_mfma_i32_16x16x32_i8 (half the rate, a quarter of the registers per
+// partial), which leaves room to pipeline MFMA and epilogue inside a wave.
 //
 // Scale epilogue (the binding cost).  Each 32x32 int32 partial needs its
 // two per-block scales applied and must be accumulated in binary32.  The
@@ -607,13 +609,10 @@ struct TileConfig {
 // Compiled tile configurations.  Occupancy hint = waves per SIMD the
 // register allocation must allow.
 const TileConfig kTiles[] = {
-    {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2>, 4>},   // 0: 8 waves 32x64, KBS 4, 2 bufs
-    {128, 128, launch_tile<Tile<128, 128, 4, 2, 2, 2>, 4>},   // 1: 8 waves 32x64, KBS 2, 2 bufs
-    {64, 128, launch_tile<Tile<64, 128, 2, 2, 2, 2>, 4>},     // 2: 4 waves 32x64, KBS 2, 2 bufs
-    {128, 128, launch_tile<Tile<128, 128, 4, 2, 2, 3>, 4>},   // 3: 8 waves 32x64, KBS 2, 3 bufs
-    {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2, 16>, 4>},   // 4: as 0 on 16x16 MFMAs
-    {128, 128, launch_tile<Tile<128, 128, 4, 2, 2, 2, 16>, 4>},   // 5: as 1 on 16x16 MFMAs
-    {64, 128, launch_tile<Tile<64, 128, 2, 2, 2, 2, 16>, 4>},     // 6: as 2 on 16x16 MFMAs
+    {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2>, 4>},       // 0: 8 waves 32x64, KBS 4
+    {64, 128, launch_tile<Tile<64, 128, 2, 2, 2, 2>, 4>},         // 1: 4 waves 32x64, KBS 2
+    {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2, 16>, 4>},   // 2: as 0 on 16x16 MFMAs
+    {128, 256, launch_tile<Tile<128, 256, 4, 4, 4, 2>, 4>},       // 3: 16 waves 32x64
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -623,9 +622,10 @@ int pick_tile(int64_t M, int64_t N) {
     const int t = atoi(e);
     if (t >= 0 && t < kNumTiles) return t;
   }
-  (void)M;
-  (void)N;
-  return 0;
+  // 128x128 tiles, unless that leaves CUs idle (fewer tiles than the 256
+  // CUs): then 64x128 tiles double the workgroup count.
+  const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
+  return tiles128 < 256 ? 1 : 0;
 }
 
 }  // namespace

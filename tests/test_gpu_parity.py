@@ -158,6 +158,23 @@ def test_gemm_parity_small(orc, M, N, K):
     check_close(C, C_ref, absdot, K, "M%d N%d K%d" % (M, N, K))
 
 
+# Every compiled tile configuration of the matrix-core kernel (the default
+# choice depends on the shape), forced through its benchmarking switch, on
+# shapes with ragged M, N and K-stage tails.
+TILE_SHAPES = [(9, 64, 32), (130, 200, 544), (300, 330, 2080), (257, 520, 1056)]
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+@pytest.mark.parametrize("M,N,K", TILE_SHAPES)
+def test_gemm_parity_every_tile(orc, monkeypatch, tile, M, N, K):
+    monkeypatch.setenv("Q8_GEMM_TILE", str(tile))
+    qa, da, qw, dw = _problem(M, N, K, 5 * M + 3 * N + K + tile)
+    say("gemm tile %d M=%d N=%d K=%d" % (tile, M, N, K))
+    C = _run(qa, da, orc.blocks_from_qd(qw, dw), N, K).cpu().numpy()
+    C_ref, absdot = orc.gemm(qa, da, qw, dw)
+    check_close(C, C_ref, absdot, K, "tile %d M%d N%d K%d" % (tile, M, N, K))
+
+
 def test_gemm_tiny_workload_every_m(orc):
     """The tiny workload, through the quantiser, at every M from 1 to 16
     (1..8 take the decode kernel, 9..16 the matrix-core kernel)."""
