@@ -175,6 +175,19 @@ def test_gemm_parity_every_tile(orc, monkeypatch, tile, M, N, K):
     check_close(C, C_ref, absdot, K, "tile %d M%d N%d K%d" % (tile, M, N, K))
 
 
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("M,N,K", [(1, 70, 96), (3, 200, 1056), (8, 130, 2080), (5, 64, 32)])
+def test_gemv_parity_every_config(orc, monkeypatch, cfg, M, N, K):
+    """Every configuration of the decode kernel (forced through its
+    benchmarking switch)."""
+    monkeypatch.setenv("Q8_GEMV_CFG", str(cfg))
+    qa, da, qw, dw = _problem(M, N, K, 11 * M + N + K + cfg)
+    say("gemv cfg %d M=%d N=%d K=%d" % (cfg, M, N, K))
+    C = _run(qa, da, orc.blocks_from_qd(qw, dw), N, K).cpu().numpy()
+    C_ref, absdot = orc.gemm(qa, da, qw, dw)
+    check_close(C, C_ref, absdot, K, "gemv cfg %d M%d N%d K%d" % (cfg, M, N, K))
+
+
 def test_gemm_tiny_workload_every_m(orc):
     """The tiny workload, through the quantiser, at every M from 1 to 16
     (1..8 take the decode kernel, 9..16 the matrix-core kernel)."""
