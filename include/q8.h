@@ -134,6 +134,34 @@ q8_status q8_gemm(int64_t M, int64_t N, int64_t K,
                   const int8_t *q_a, const uint16_t *d_a, const void *w_packed,
                   float *C, int64_t ldc, void *stream);
 
+/*
+ * q8_gemm_act -- quantise activation rows and multiply: C = A * W^T with A
+ * quantised on the fly (q8_quantize_act followed by q8_gemm, in one call).
+ *
+ * Operation: exactly that of q8_quantize_act on x, then q8_gemm on its
+ * output.  For M <= 8 (decode) one kernel does both: every workgroup
+ * quantises the activation blocks it needs as it streams the weights, so
+ * the quantised rows never go through memory; C, and q_a/d_a when given,
+ * are bit-identical to the two separate calls.  For M > 8 the two kernels
+ * run one after the other on the stream, through q_a/d_a.  (The source
+ * engine quantises activations on the fly for its int8 GEMM; see the note
+ * at the top.)
+ *
+ * x, dtype, ldx  as for q8_quantize_act (16-byte aligned, ldx*elem % 16 == 0).
+ * w_packed, N, C, ldc  as for q8_gemm.
+ * q_a, d_a  [M][K] int8 and [M][K/32] binary16 outputs: both NULL or both
+ *       set (16-byte and 2-byte aligned).  Optional for M <= 8 (not written
+ *       when NULL); required for M > 8, where they hold the quantised rows
+ *       between the two kernels.
+ *
+ * Errors: Q8_ERR_NULL (x, w_packed or C NULL; only one of q_a/d_a; q_a NULL
+ * with M > 8), Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DTYPE, Q8_ERR_DEVICE,
+ * Q8_ERR_LAUNCH.
+ */
+q8_status q8_gemm_act(const void *x, q8_dtype dtype, int64_t M, int64_t N, int64_t K,
+                      int64_t ldx, const void *w_packed, float *C, int64_t ldc,
+                      int8_t *q_a, uint16_t *d_a, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *q8_status_string(q8_status s);
 

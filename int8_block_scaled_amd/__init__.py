@@ -10,6 +10,7 @@ The calls keep the C names:
 * ``q8_pack_weights(w_blocks, N, K)``  GGUF Q8_0 blocks -> packed layout
 * ``q8_quantize_act(x, K=None)``       fp32/bf16 rows -> (int8 q, fp16 d)
 * ``q8_gemm(q_a, d_a, w_packed, N, K)``  C = A W^T in fp32
+* ``q8_gemm_act(x, w_packed, N, K)``  quantise x on the fly, then C = A W^T
 """
 import ctypes
 import functools
@@ -23,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libq8gemm.so")
 Q8_F32, Q8_BF16 = 0, 1
 STATUS = {0: "Q8_OK", 1: "Q8_ERR_NULL", 2: "Q8_ERR_SHAPE", 3: "Q8_ERR_ALIGN",
           4: "Q8_ERR_DTYPE", 5: "Q8_ERR_SIZE", 6: "Q8_ERR_DEVICE", 7: "Q8_ERR_LAUNCH"}
-EXPORTS = ("q8_pack_weights", "q8_quantize_act", "q8_gemm", "q8_status_string")
+EXPORTS = ("q8_pack_weights", "q8_quantize_act", "q8_gemm", "q8_gemm_act", "q8_status_string")
 
 _lib = None
 
@@ -51,6 +52,8 @@ def _load():
         L.q8_quantize_act.restype = ctypes.c_int
         L.q8_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, i64, vp]
         L.q8_gemm.restype = ctypes.c_int
+        L.q8_gemm_act.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, i64, vp, vp, vp]
+        L.q8_gemm_act.restype = ctypes.c_int
         L.q8_status_string.argtypes = [ctypes.c_int]
         L.q8_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -104,6 +107,14 @@ def q8_pack_weights(w_blocks: torch.Tensor, N: int, K: int, out: torch.Tensor = 
     return out
 
 
+def _act_dtype(x):
+    if x.dtype == torch.float32:
+        return Q8_F32
+    if x.dtype == torch.bfloat16:
+        return Q8_BF16
+    raise TypeError("x must be float32 or bfloat16")
+
+
 def q8_quantize_act(x: torch.Tensor, K: int = None, q: torch.Tensor = None,
                     d: torch.Tensor = None):
     """Rows of x (float32 or bfloat16, [M][ldx], unit column stride) ->
@@ -111,12 +122,7 @@ def q8_quantize_act(x: torch.Tensor, K: int = None, q: torch.Tensor = None,
     _need_cuda("x", x)
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
-    if x.dtype == torch.float32:
-        dt = Q8_F32
-    elif x.dtype == torch.bfloat16:
-        dt = Q8_BF16
-    else:
-        raise TypeError("x must be float32 or bfloat16")
+    dt = _act_dtype(x)
     M = x.shape[0]
     K = x.shape[1] if K is None else K
     ldx = x.stride(0) if M > 1 else max(x.stride(0), K)
@@ -150,4 +156,38 @@ def q8_gemm(q_a: torch.Tensor, d_a: torch.Tensor, w_packed: torch.Tensor, N: int
     ldc = out.stride(0) if M > 1 else max(out.stride(0), N)
     _check("q8_gemm", _load().q8_gemm(M, N, K, _ptr(q_a), _ptr(d_a), _ptr(w_packed),
                                       _ptr(out), ldc, _stream(q_a)))
+    return out
+
+
+def q8_gemm_act(x: torch.Tensor, w_packed: torch.Tensor, N: int, K: int = None,
+                out: torch.Tensor = None, q: torch.Tensor = None, d: torch.Tensor = None):
+    """C[M][N] float32 for activation rows x (float32 or bfloat16, [M][ldx]),
+    quantised on the fly.  q/d (int8 [M][K], float16 [M][K/32]) receive the
+    quantised rows when given; for M > 8 they are allocated here if absent
+    (the two kernels exchange the rows through them)."""
+    _need_cuda("x", x)
+    _need_cuda("w_packed", w_packed)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    dt = _act_dtype(x)
+    M = x.shape[0]
+    K = x.shape[1] if K is None else K
+    ldx = x.stride(0) if M > 1 else max(x.stride(0), K)
+    if w_packed.numel() < q8_packed_bytes(N, K):
+        raise ValueError("w_packed is smaller than the packed layout for N=%d K=%d" % (N, K))
+    if (q is None) != (d is None):
+        raise ValueError("give both q and d, or neither")
+    if q is None and M > 8:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        d = torch.empty((M, K // 32), dtype=torch.float16, device=x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if out.dtype != torch.float32 or out.dim() != 2 or out.stride(1) != 1 or out.shape[1] < N \
+            or out.shape[0] != M:
+        raise TypeError("out must be float32 [M][>=N] with unit column stride")
+    ldc = out.stride(0) if M > 1 else max(out.stride(0), N)
+    qp = _ptr(q) if q is not None else None
+    dp = _ptr(d) if d is not None else None
+    _check("q8_gemm_act", _load().q8_gemm_act(_ptr(x), dt, M, N, K, ldx, _ptr(w_packed),
+                                              _ptr(out), ldc, qp, dp, _stream(x)))
     return out

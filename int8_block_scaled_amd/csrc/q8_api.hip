@@ -118,4 +118,34 @@ q8_status q8_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint
   return e == hipSuccess ? Q8_OK : Q8_ERR_LAUNCH;
 }
 
+q8_status q8_gemm_act(const void* x, q8_dtype dtype, int64_t M, int64_t N, int64_t K,
+                      int64_t ldx, const void* w_packed, float* C, int64_t ldc, int8_t* q_a,
+                      uint16_t* d_a, void* stream) {
+  if (dtype != Q8_F32 && dtype != Q8_BF16) return Q8_ERR_DTYPE;
+  if (M < 0 || N < 1 || N >= kMaxDim || !valid_k(K) || ldx < K || ldc < N) return Q8_ERR_SHAPE;
+  if (M == 0) return Q8_OK;
+  if (x == nullptr || w_packed == nullptr || C == nullptr) return Q8_ERR_NULL;
+  // q_a and d_a: both or neither; required above the decode size
+  if ((q_a == nullptr) != (d_a == nullptr)) return Q8_ERR_NULL;
+  if (M > q8::kGemvMaxM && q_a == nullptr) return Q8_ERR_NULL;
+  const int64_t esize = dtype == Q8_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(w_packed, 16) || !aligned(C, 4))
+    return Q8_ERR_ALIGN;
+  if (q_a != nullptr && (!aligned(q_a, 16) || !aligned(d_a, 2))) return Q8_ERR_ALIGN;
+  if (M * (K / q8::kQK) * 4 / 256 >= kMaxDim) return Q8_ERR_SHAPE;
+  if (((M + 127) / 128) * ((N + 127) / 128) >= kMaxDim) return Q8_ERR_SHAPE;
+  const q8_status dev = check_device();
+  if (dev != Q8_OK) return dev;
+  const uint8_t* wp = static_cast<const uint8_t*>(w_packed);
+  hipError_t e;
+  if (M <= q8::kGemvMaxM) {
+    e = q8::launch_gemv_act(static_cast<int>(M), x, static_cast<int>(dtype), ldx, N, K, wp, C,
+                            ldc, q_a, d_a, as_stream(stream));
+  } else {
+    e = q8::launch_quantize(x, static_cast<int>(dtype), M, K, ldx, q_a, d_a, as_stream(stream));
+    if (e == hipSuccess) e = q8::launch_gemm(M, N, K, q_a, d_a, wp, C, ldc, as_stream(stream));
+  }
+  return e == hipSuccess ? Q8_OK : Q8_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -110,6 +110,120 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(
   }
 }
 
+// Fused decode step: the same product, from unquantised activation rows x
+// (binary32 or bfloat16).  Every wave quantises the activation blocks of its
+// chunk itself (quantize8, the code of the quantise kernel, so codes and
+// scales are bit-identical to it), right after issuing the chunk's weight
+// loads so that the two loads overlap, and keeps them in a small LDS slot
+// of its own: codes [m][i][32] and scales [m][i] for the L blocks i of the
+// chunk.  Lanes then read them back with broadcast LDS loads.  The block
+// walk, the dot products and the reduction are those of gemv_q8_kernel, so
+// C is bit-identical to quantising first and then running that kernel.
+// Workgroup 0 also stores the codes and scales when q_out is not NULL.
+template <int MR, int L, bool kBf16>
+__global__ __launch_bounds__(kThreads) void gemv_q8_act_kernel(
+    const void* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wq,
+    const uint16_t* __restrict__ ws, float* __restrict__ C, int64_t N, int64_t K, int64_t KB,
+    int64_t ldc, int kb_per_wave, int8_t* __restrict__ q_out, uint16_t* __restrict__ d_out) {
+  constexpr int kSlotBytes = MR * L * (kQK + 4);   // per wave: codes, then binary32 scales
+  constexpr int kItems = MR * L * 4;               // quantiser lanes per chunk (4 per block)
+  constexpr int kPasses = (kItems + 63) / 64;
+  __shared__ __align__(16) uint8_t lds[kMaxWaves * (kSlotBytes > MR * 256 ? kSlotBytes : MR * 256)];
+  const int64_t g = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int64_t kb0 = static_cast<int64_t>(wave) * kb_per_wave;
+  const int64_t kb1 = kb0 + kb_per_wave < KB ? kb0 + kb_per_wave : KB;
+  const bool store_q = q_out != nullptr && blockIdx.x == 0;
+
+  uint8_t* const qslot = lds + wave * kSlotBytes;
+  float* const dslot = reinterpret_cast<float*>(qslot + MR * L * kQK);
+
+  const v4u* wp = reinterpret_cast<const v4u*>(wq + g * KB * kGroupBlockBytes) + lane;
+  const uint16_t* sp = ws + g * KB * kGroupRows + lane;
+
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+
+  for (int64_t c = kb0; c < kb1; c += L) {
+    v4u w0[L], w1[L];
+    float dw[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int64_t kb = (c + i < kb1) ? c + i : kb1 - 1;
+      w0[i] = __builtin_nontemporal_load(wp + (kb * 2 + 0) * 64);
+      w1[i] = __builtin_nontemporal_load(wp + (kb * 2 + 1) * 64);
+      dw[i] = f16_bits_to_f32(sp[kb * kGroupRows]) * (c + i < kb1 ? 1.0f : 0.0f);
+    }
+    // Quantise the chunk's activation blocks: item t = (m * L + i) * 4 + sub.
+    float v[kPasses][8];
+#pragma unroll
+    for (int u = 0; u < kPasses; ++u) {
+      const int t = u * 64 + lane;
+      const int m = t / (L * 4), i = (t / 4) % L, sub = t % 4;
+      const int64_t kb = (c + i < kb1) ? c + i : kb1 - 1;
+      if (t < kItems) {
+        load8<kBf16>(x, m * ldx + kb * kQK + sub * 8, v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPasses; ++u) {
+      const int t = u * 64 + lane;
+      const int m = t / (L * 4), i = (t / 4) % L, sub = t % 4;
+      uint32_t lo, hi;
+      uint16_t dbits;
+      quantize8(v[u], lo, hi, dbits);   // all lanes take part (lane exchanges)
+      if (t < kItems) {
+        *reinterpret_cast<uint2*>(qslot + (m * L + i) * kQK + sub * 8) = make_uint2(lo, hi);
+        if (sub == 0) dslot[m * L + i] = f16_bits_to_f32(dbits);
+        if (store_q && c + i < kb1) {
+          *reinterpret_cast<uint2*>(q_out + m * K + (c + i) * kQK + sub * 8) = make_uint2(lo, hi);
+          if (sub == 0) d_out[m * KB + c + i] = dbits;
+        }
+      }
+    }
+    // The slot is this wave's alone and a wave's LDS accesses complete in
+    // order: no barrier is needed before reading it back.
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const v4u* ap = reinterpret_cast<const v4u*>(qslot + (m * L + i) * kQK);
+        const v4u a0 = ap[0], a1 = ap[1];
+        int p = 0;
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w0[i].x), static_cast<int>(a0.x), p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w0[i].y), static_cast<int>(a0.y), p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w0[i].z), static_cast<int>(a0.z), p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w0[i].w), static_cast<int>(a0.w), p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w1[i].x), static_cast<int>(a1.x), p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w1[i].y), static_cast<int>(a1.y), p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w1[i].z), static_cast<int>(a1.z), p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w1[i].w), static_cast<int>(a1.w), p, false);
+        const float s = dw[i] * dslot[m * L + i];   // exact: 11 x 11 bits
+        acc[m] = fmaf(static_cast<float>(p), s, acc[m]);
+      }
+    }
+  }
+
+  __syncthreads();   // every wave is done with its slot: reuse LDS for the partials
+  float* red = reinterpret_cast<float*>(lds);   // [wave][m][lane]
+#pragma unroll
+  for (int m = 0; m < MR; ++m) red[(wave * MR + m) * 64 + lane] = acc[m];
+  __syncthreads();
+  for (int t = threadIdx.x; t < MR * 64; t += blockDim.x) {
+    const int m = t >> 6, r = t & 63;
+    float sum = 0.0f;
+    for (int w = 0; w < nwaves; ++w) sum += red[(w * MR + m) * 64 + r];
+    const int64_t n = g * kGroupRows + r;
+    if (n < N) C[m * ldc + n] = sum;
+  }
+}
+
 template <int MR, int L, bool NT>
 hipError_t launch_m(int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                     const uint8_t* w_packed, float* C, int64_t ldc, int max_waves,
@@ -139,7 +253,45 @@ hipError_t launch_cfg(int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d
   }
 }
 
+template <int MR>
+hipError_t launch_act_m(const void* x, bool bf16, int64_t ldx, int64_t N, int64_t K,
+                        const uint8_t* w_packed, float* C, int64_t ldc, int8_t* q_out,
+                        uint16_t* d_out, hipStream_t stream) {
+  constexpr int L = 4;   // as the default configuration of the unfused kernel
+  const int64_t KB = K / kQK;
+  const int64_t NG = num_groups(N);
+  const int waves = static_cast<int>(KB < kMaxWaves ? KB : kMaxWaves);
+  const int kb_per_wave = static_cast<int>((KB + waves - 1) / waves);
+  const uint16_t* ws = reinterpret_cast<const uint16_t*>(w_packed + NG * KB * kGroupBlockBytes);
+  if (bf16)
+    hipLaunchKernelGGL((gemv_q8_act_kernel<MR, L, true>), dim3(static_cast<uint32_t>(NG)),
+                       dim3(waves * 64), 0, stream, x, ldx, w_packed, ws, C, N, K, KB, ldc,
+                       kb_per_wave, q_out, d_out);
+  else
+    hipLaunchKernelGGL((gemv_q8_act_kernel<MR, L, false>), dim3(static_cast<uint32_t>(NG)),
+                       dim3(waves * 64), 0, stream, x, ldx, w_packed, ws, C, N, K, KB, ldc,
+                       kb_per_wave, q_out, d_out);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_gemv_act(int M, const void* x, int dtype, int64_t ldx, int64_t N, int64_t K,
+                           const uint8_t* w_packed, float* C, int64_t ldc, int8_t* q_out,
+                           uint16_t* d_out, hipStream_t stream) {
+  const bool bf16 = dtype == 1;
+  switch (M) {
+    case 1: return launch_act_m<1>(x, bf16, ldx, N, K, w_packed, C, ldc, q_out, d_out, stream);
+    case 2: return launch_act_m<2>(x, bf16, ldx, N, K, w_packed, C, ldc, q_out, d_out, stream);
+    case 3: return launch_act_m<3>(x, bf16, ldx, N, K, w_packed, C, ldc, q_out, d_out, stream);
+    case 4: return launch_act_m<4>(x, bf16, ldx, N, K, w_packed, C, ldc, q_out, d_out, stream);
+    case 5: return launch_act_m<5>(x, bf16, ldx, N, K, w_packed, C, ldc, q_out, d_out, stream);
+    case 6: return launch_act_m<6>(x, bf16, ldx, N, K, w_packed, C, ldc, q_out, d_out, stream);
+    case 7: return launch_act_m<7>(x, bf16, ldx, N, K, w_packed, C, ldc, q_out, d_out, stream);
+    case 8: return launch_act_m<8>(x, bf16, ldx, N, K, w_packed, C, ldc, q_out, d_out, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gemv(int M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                        const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {

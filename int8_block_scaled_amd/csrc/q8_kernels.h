@@ -28,6 +28,11 @@ hipError_t launch_gemv(int M, int64_t N, int64_t K, const int8_t* q_a, const uin
                        const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream);
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                        const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream);
+// Fused decode step (M <= kGemvMaxM): quantise x and multiply; q_out/d_out
+// may be NULL, else they receive the quantised rows.
+hipError_t launch_gemv_act(int M, const void* x, int dtype, int64_t ldx, int64_t N, int64_t K,
+                           const uint8_t* w_packed, float* C, int64_t ldc, int8_t* q_out,
+                           uint16_t* d_out, hipStream_t stream);
 
 constexpr int kGemvMaxM = 8;       // M <= kGemvMaxM takes the decode kernel
 
@@ -42,6 +47,67 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
 // (v_cvt_f16_f32 under the default rounding and denormal modes).
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// ---------------------------------------------------------------------------
+// The Q8_0 block quantiser, shared by the quantise kernel and the fused
+// decode kernel so that both produce the same bits.  Four consecutive,
+// 4-aligned lanes of a wave hold the 32 values of one block, eight each.
+//
+// Bit-exactness: d32 = amax/127 and id = 1/d32 use the correctly rounded
+// binary32 division (HIP's default; never build with fast-math or
+// -fno-hip-fp32-correctly-rounded-divide-sqrt), v = x*id is a single
+// multiply, roundf rounds half away from zero, and the binary16 conversion
+// is v_cvt_f16_f32 (round to nearest even, binary16 subnormals kept).
+// ---------------------------------------------------------------------------
+
+// Eight consecutive values of row data x (binary32, or bfloat16 widened
+// exactly) starting at element off.
+template <bool kBf16>
+__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t off, float v[8]) {
+  if constexpr (kBf16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// Quantise the lane's eight values of a block: codes packed little-endian
+// into lo (values 0..3) and hi (4..7), and the block's binary16 scale bits.
+// Blocks with d32 < FLT_MIN (all zero, or a binary32-subnormal scale) give
+// zero codes and d = +0.  All four lanes of every block must be active.
+__device__ __forceinline__ void quantize8(const float v[8], uint32_t& lo, uint32_t& hi,
+                                          uint16_t& dbits) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 4));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 4));
+  const float d32 = amax / 127.0f;
+  lo = 0;
+  hi = 0;
+  dbits = 0;
+  if (d32 >= 1.17549435e-38f) {   // FLT_MIN
+    const float id = 1.0f / d32;
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int qi = static_cast<int>(roundf(v[i] * id));  // |qi| <= 127
+      b[i] = static_cast<uint32_t>(qi) & 0xffu;
+    }
+    lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    dbits = f32_to_f16_bits(d32);
+  }
 }
 
 }  // namespace q8

@@ -91,6 +91,30 @@ def test_gemm_validation(L):
     assert L.q8_gemm(4, 64, 64, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10002), 64, None) == ALIGN
 
 
+def test_gemm_act_validation(L):
+    f = L.q8_gemm_act
+    #        x     dt  M   N   K   ldx  w     C     ldc  q     d
+    assert f(FAKE, 2, 4, 64, 64, 64, FAKE, FAKE, 64, None, None, None) == DTYPE
+    assert f(FAKE, 0, -1, 64, 64, 64, FAKE, FAKE, 64, None, None, None) == SHAPE
+    assert f(FAKE, 0, 4, 0, 64, 64, FAKE, FAKE, 64, None, None, None) == SHAPE
+    assert f(FAKE, 0, 4, 64, 48, 64, FAKE, FAKE, 64, None, None, None) == SHAPE
+    assert f(FAKE, 0, 4, 64, 64, 32, FAKE, FAKE, 64, None, None, None) == SHAPE      # ldx < K
+    assert f(FAKE, 0, 4, 64, 64, 64, FAKE, FAKE, 63, None, None, None) == SHAPE      # ldc < N
+    assert f(None, 0, 0, 64, 64, 64, None, None, 64, None, None, None) == OK         # M == 0
+    assert f(None, 0, 4, 64, 64, 64, FAKE, FAKE, 64, None, None, None) == NULL
+    assert f(FAKE, 0, 4, 64, 64, 64, None, FAKE, 64, None, None, None) == NULL
+    assert f(FAKE, 0, 4, 64, 64, 64, FAKE, None, 64, None, None, None) == NULL
+    assert f(FAKE, 0, 4, 64, 64, 64, FAKE, FAKE, 64, FAKE, None, None) == NULL       # q without d
+    assert f(FAKE, 0, 4, 64, 64, 64, FAKE, FAKE, 64, None, FAKE, None) == NULL       # d without q
+    assert f(FAKE, 0, 9, 64, 64, 64, FAKE, FAKE, 64, None, None, None) == NULL       # M > 8 needs q, d
+    assert f(ODD, 0, 4, 64, 64, 64, FAKE, FAKE, 64, None, None, None) == ALIGN
+    assert f(FAKE, 0, 4, 64, 64, 66, FAKE, FAKE, 64, None, None, None) == ALIGN      # pitch 264 B
+    assert f(FAKE, 0, 4, 64, 64, 64, ODD, FAKE, 64, None, None, None) == ALIGN
+    assert f(FAKE, 0, 4, 64, 64, 64, FAKE, ctypes.c_void_p(0x10002), 64, None, None, None) == ALIGN
+    assert f(FAKE, 0, 4, 64, 64, 64, FAKE, FAKE, 64, ODD, FAKE, None) == ALIGN
+    assert f(FAKE, 0, 4, 64, 64, 64, FAKE, FAKE, 64, FAKE, ODD, None) == ALIGN
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
