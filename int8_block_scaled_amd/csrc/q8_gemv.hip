@@ -13,10 +13,12 @@
 // does the int8 dots on the vector ALU (v_dot4_i32_i8), not on the matrix
 // cores.
 //
-// Work split: one workgroup per 64-row group; its (up to 16) waves split the
-// K blocks evenly and walk their range in chunks of L blocks, all of a
-// chunk's loads in flight together.  Lane l of a wave owns row 64g + l.  In a piece (g, kb, h) lane l
-// holds bytes [16h, 16h+16) of its row's block kb, so all 64 lanes need the
+// Work split: a workgroup owns up to 64 rows (a whole 64-row group in
+// gemv_q8_kernel; a slice sized so the grid fills every CU in the default,
+// gemv_q8_slice_kernel); its (up to 16) waves split the K blocks evenly and
+// walk their range in chunks of L blocks, all of a chunk's loads in flight
+// together.  Lane l of a wave owns one row.  In a piece (g, kb, h) a lane
+// holds bytes [16h, 16h+16) of its row's block kb, so all lanes need the
 // same 16 activation bytes: those are wave-uniform and come from scalar
 // loads into SGPRs, which v_dot4 takes as its second operand.  A lane has
 // both halves of its block, so the block dot is an exact int32 in one lane
@@ -110,6 +112,108 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(
   }
 }
 
+// Row-slice variant: a workgroup owns R <= 64 consecutive rows (a slice that
+// may straddle two 64-row groups) instead of one whole group, with R chosen
+// so that the grid fills every CU (N = 12288: R = 48, 256 workgroups for
+// 256 CUs instead of 192).  Lane l < R owns row R*w + l and computes its
+// piece addresses itself; lanes past R (or past N) re-read a row of the
+// slice (same lines, no extra HBM traffic) and are dropped.  Everything else is as in
+// gemv_q8_kernel: chunks of L blocks, wave-uniform activations in SGPRs,
+// exact block dots, waves added in a fixed order.
+template <int MR, int L>
+__global__ __launch_bounds__(kThreads) void gemv_q8_slice_kernel(
+    const int8_t* __restrict__ q_a, const uint16_t* __restrict__ d_a,
+    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
+    float* __restrict__ C, int64_t N, int64_t K, int64_t KB, int64_t ldc, int kb_per_wave,
+    int rows) {
+  __shared__ float red[kMaxWaves][MR][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int64_t kb0 = static_cast<int64_t>(wave) * kb_per_wave;
+  const int64_t kb1 = kb0 + kb_per_wave < KB ? kb0 + kb_per_wave : KB;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * rows;
+  // the row this lane loads: its own, or the slice's last; never past N - 1
+  // (when N is a multiple of 64 the packed layout has no padding rows)
+  int64_t n = n0 + (lane < rows ? lane : rows - 1);
+  n = n < N ? n : N - 1;
+  const int64_t g = n >> 6, r = n & 63;
+
+  const v4u* wp = reinterpret_cast<const v4u*>(wq + g * KB * kGroupBlockBytes) + r;
+  const uint16_t* sp = ws + g * KB * kGroupRows + r;
+
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+
+  for (int64_t c = kb0; c < kb1; c += L) {
+    v4u w0[L], w1[L];
+    float dw[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int64_t kb = (c + i < kb1) ? c + i : kb1 - 1;
+      w0[i] = __builtin_nontemporal_load(wp + (kb * 2 + 0) * 64);
+      w1[i] = __builtin_nontemporal_load(wp + (kb * 2 + 1) * 64);
+      dw[i] = f16_bits_to_f32(sp[kb * kGroupRows]) * (c + i < kb1 ? 1.0f : 0.0f);
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int64_t kb = (c + i < kb1) ? c + i : kb1 - 1;
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const int* a = reinterpret_cast<const int*>(q_a + m * K + kb * kQK);  // wave-uniform
+        int p = 0;
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w0[i].x), a[0], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w0[i].y), a[1], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w0[i].z), a[2], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w0[i].w), a[3], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w1[i].x), a[4], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w1[i].y), a[5], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w1[i].z), a[6], p, false);
+        p = __builtin_amdgcn_sdot4(static_cast<int>(w1[i].w), a[7], p, false);
+        const float s = dw[i] * f16_bits_to_f32(d_a[m * KB + kb]);  // exact: 11 x 11 bits
+        acc[m] = fmaf(static_cast<float>(p), s, acc[m]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int m = 0; m < MR; ++m) red[wave][m][lane] = acc[m];
+  __syncthreads();
+  for (int t = threadIdx.x; t < MR * 64; t += blockDim.x) {
+    const int m = t >> 6, l = t & 63;
+    if (l >= rows) continue;
+    float sum = 0.0f;
+    for (int w = 0; w < nwaves; ++w) sum += red[w][m][l];
+    const int64_t nn = n0 + l;
+    if (nn < N) C[m * ldc + nn] = sum;
+  }
+}
+
+// Rows per workgroup of the slice kernels: enough workgroups for the 256
+// CUs, a multiple of 8, at most one 64-row group.
+inline int slice_rows(int64_t N) {
+  int64_t rows = (N + 255) / 256;
+  rows = ((rows + 7) / 8) * 8;
+  return static_cast<int>(rows > kGroupRows ? kGroupRows : rows);
+}
+
+template <int MR, int L>
+hipError_t launch_slice(int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
+                        const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
+  const int64_t KB = K / kQK;
+  const int64_t NG = num_groups(N);
+  const int waves = static_cast<int>(KB < kMaxWaves ? KB : kMaxWaves);
+  const int kb_per_wave = static_cast<int>((KB + waves - 1) / waves);
+  const int rows = slice_rows(N);
+  const int64_t grid = (N + rows - 1) / rows;
+  const uint16_t* ws = reinterpret_cast<const uint16_t*>(w_packed + NG * KB * kGroupBlockBytes);
+  hipLaunchKernelGGL((gemv_q8_slice_kernel<MR, L>), dim3(static_cast<uint32_t>(grid)),
+                     dim3(waves * 64), 0, stream, q_a, d_a, w_packed, ws, C, N, K, KB, ldc,
+                     kb_per_wave, rows);
+  return hipGetLastError();
+}
+
 // Fused decode step: the same product, from unquantised activation rows x
 // (binary32 or bfloat16).  Every wave quantises the activation blocks of its
 // chunk itself (quantize8, the code of the quantise kernel, so codes and
@@ -124,24 +228,29 @@ template <int MR, int L, bool kBf16>
 __global__ __launch_bounds__(kThreads) void gemv_q8_act_kernel(
     const void* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ ws, float* __restrict__ C, int64_t N, int64_t K, int64_t KB,
-    int64_t ldc, int kb_per_wave, int8_t* __restrict__ q_out, uint16_t* __restrict__ d_out) {
+    int64_t ldc, int kb_per_wave, int rows, int8_t* __restrict__ q_out,
+    uint16_t* __restrict__ d_out) {
   constexpr int kSlotBytes = MR * L * (kQK + 4);   // per wave: codes, then binary32 scales
   constexpr int kItems = MR * L * 4;               // quantiser lanes per chunk (4 per block)
   constexpr int kPasses = (kItems + 63) / 64;
   __shared__ __align__(16) uint8_t lds[kMaxWaves * (kSlotBytes > MR * 256 ? kSlotBytes : MR * 256)];
-  const int64_t g = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
   const int64_t kb0 = static_cast<int64_t>(wave) * kb_per_wave;
   const int64_t kb1 = kb0 + kb_per_wave < KB ? kb0 + kb_per_wave : KB;
   const bool store_q = q_out != nullptr && blockIdx.x == 0;
+  // rows as in gemv_q8_slice_kernel
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * rows;
+  int64_t n = n0 + (lane < rows ? lane : rows - 1);
+  n = n < N ? n : N - 1;
+  const int64_t g = n >> 6, r = n & 63;
 
   uint8_t* const qslot = lds + wave * kSlotBytes;
   float* const dslot = reinterpret_cast<float*>(qslot + MR * L * kQK);
 
-  const v4u* wp = reinterpret_cast<const v4u*>(wq + g * KB * kGroupBlockBytes) + lane;
-  const uint16_t* sp = ws + g * KB * kGroupRows + lane;
+  const v4u* wp = reinterpret_cast<const v4u*>(wq + g * KB * kGroupBlockBytes) + r;
+  const uint16_t* sp = ws + g * KB * kGroupRows + r;
 
   float acc[MR];
 #pragma unroll
@@ -216,11 +325,12 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_act_kernel(
   for (int m = 0; m < MR; ++m) red[(wave * MR + m) * 64 + lane] = acc[m];
   __syncthreads();
   for (int t = threadIdx.x; t < MR * 64; t += blockDim.x) {
-    const int m = t >> 6, r = t & 63;
+    const int m = t >> 6, l = t & 63;
+    if (l >= rows) continue;
     float sum = 0.0f;
-    for (int w = 0; w < nwaves; ++w) sum += red[(w * MR + m) * 64 + r];
-    const int64_t n = g * kGroupRows + r;
-    if (n < N) C[m * ldc + n] = sum;
+    for (int w = 0; w < nwaves; ++w) sum += red[(w * MR + m) * 64 + l];
+    const int64_t nn = n0 + l;
+    if (nn < N) C[m * ldc + nn] = sum;
   }
 }
 
@@ -241,15 +351,17 @@ hipError_t launch_m(int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a
 template <int MR>
 hipError_t launch_cfg(int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                       const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
-  // Q8_GEMV_CFG=<c> (benchmarking aid): c = 0: 16 waves x chunks of 4
-  // blocks, nontemporal weight loads (default); 1: the same with ordinary
-  // loads; 2: 16 waves x chunks of 8, nontemporal.
+  // Q8_GEMV_CFG=<c> (benchmarking aid): c = 0: row slices sized to fill
+  // the CUs, 16 waves x chunks of 4 blocks, nontemporal weight loads
+  // (default); 1: one workgroup per 64-row group, otherwise the same; 2: as
+  // 1 with ordinary loads; 3: as 1 with chunks of 8.
   int cfg = 0;
   if (const char* e = getenv("Q8_GEMV_CFG")) cfg = atoi(e);
   switch (cfg) {
-    case 1: return launch_m<MR, 4, false>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
-    case 2: return launch_m<MR, 8, true>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
-    default: return launch_m<MR, 4, true>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
+    case 1: return launch_m<MR, 4, true>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
+    case 2: return launch_m<MR, 4, false>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
+    case 3: return launch_m<MR, 8, true>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
+    default: return launch_slice<MR, 4>(N, K, q_a, d_a, w_packed, C, ldc, stream);
   }
 }
 
@@ -262,15 +374,19 @@ hipError_t launch_act_m(const void* x, bool bf16, int64_t ldx, int64_t N, int64_
   const int64_t NG = num_groups(N);
   const int waves = static_cast<int>(KB < kMaxWaves ? KB : kMaxWaves);
   const int kb_per_wave = static_cast<int>((KB + waves - 1) / waves);
+  // Every workgroup quantises the whole activation, so above M = 4 the
+  // extra workgroups of row slices cost more than they gain: whole groups.
+  const int rows = MR > 4 ? kGroupRows : slice_rows(N);
+  const uint32_t grid = static_cast<uint32_t>((N + rows - 1) / rows);
   const uint16_t* ws = reinterpret_cast<const uint16_t*>(w_packed + NG * KB * kGroupBlockBytes);
   if (bf16)
-    hipLaunchKernelGGL((gemv_q8_act_kernel<MR, L, true>), dim3(static_cast<uint32_t>(NG)),
-                       dim3(waves * 64), 0, stream, x, ldx, w_packed, ws, C, N, K, KB, ldc,
-                       kb_per_wave, q_out, d_out);
+    hipLaunchKernelGGL((gemv_q8_act_kernel<MR, L, true>), dim3(grid), dim3(waves * 64), 0,
+                       stream, x, ldx, w_packed, ws, C, N, K, KB, ldc, kb_per_wave, rows, q_out,
+                       d_out);
   else
-    hipLaunchKernelGGL((gemv_q8_act_kernel<MR, L, false>), dim3(static_cast<uint32_t>(NG)),
-                       dim3(waves * 64), 0, stream, x, ldx, w_packed, ws, C, N, K, KB, ldc,
-                       kb_per_wave, q_out, d_out);
+    hipLaunchKernelGGL((gemv_q8_act_kernel<MR, L, false>), dim3(grid), dim3(waves * 64), 0,
+                       stream, x, ldx, w_packed, ws, C, N, K, KB, ldc, kb_per_wave, rows, q_out,
+                       d_out);
   return hipGetLastError();
 }
 
