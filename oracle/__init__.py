@@ -48,6 +48,10 @@ def _bind(L):
     L.q8ref_packed_bytes.restype = ctypes.c_size_t
     L.q8ref_pack.argtypes = [vp, i64, i64, vp]
     L.q8ref_pack.restype = None
+    L.q8ref_silu.argtypes = [ctypes.c_double]
+    L.q8ref_silu.restype = ctypes.c_double
+    L.q8ref_swiglu_quant.argtypes = [i64, i64, vp, vp, vp, vp, vp]
+    L.q8ref_swiglu_quant.restype = None
     L.q8ref_num_threads.argtypes = []
     L.q8ref_num_threads.restype = ctypes.c_int
     return L
@@ -171,6 +175,40 @@ class Oracle:
         out = np.empty(self.packed_bytes(N, K), dtype=np.uint8)
         self.L.q8ref_pack(_p(blocks), N, K, _p(out))
         return out
+
+    def silu(self, x: float) -> float:
+        return float(self.L.q8ref_silu(float(x)))
+
+    def swiglu_quant(self, G, U):
+        """Gate and up products G, U ([M][I] float64) -> (h float64 [M][I],
+        q int8 [M][I], d uint16 [M][I/32]): h = silu(G)*U, quantised per 32
+        along I."""
+        G, U = _c(G, np.float64), _c(U, np.float64)
+        M, I = G.shape
+        assert U.shape == (M, I) and I % 32 == 0
+        h = np.empty((M, I), dtype=np.float64)
+        q = np.empty((M, I), dtype=np.int8)
+        d = np.empty((M, I // 32), dtype=np.uint16)
+        self.L.q8ref_swiglu_quant(M, I, _p(G), _p(U), _p(h), _p(q), _p(d))
+        return h, q, d
+
+    @staticmethod
+    def interleave_gateup(gate_rows, up_rows):
+        """Rows of the gate and up weights ([I][...] each, I % 32 == 0) ->
+        [2I][...] in the order of the gate/up packed layout: 64-row group g
+        holds gate rows 32g..32g+31, then up rows 32g..32g+31."""
+        gate_rows, up_rows = np.asarray(gate_rows), np.asarray(up_rows)
+        I = gate_rows.shape[0]
+        assert up_rows.shape == gate_rows.shape and I % 32 == 0
+        rest = gate_rows.shape[1:]
+        g = gate_rows.reshape((I // 32, 32) + rest)
+        u = up_rows.reshape((I // 32, 32) + rest)
+        return np.ascontiguousarray(np.concatenate([g, u], axis=1).reshape((2 * I,) + rest))
+
+    def pack_gateup(self, gate_blocks, up_blocks, I, K) -> np.ndarray:
+        """GGUF Q8_0 bytes of the gate and up weights ([I][K/32*34] each) ->
+        the packed layout of their interleaved rows (2I rows)."""
+        return self.pack(self.interleave_gateup(gate_blocks, up_blocks), 2 * I, K)
 
     def num_threads(self) -> int:
         return int(self.L.q8ref_num_threads())

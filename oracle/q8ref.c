@@ -328,6 +328,41 @@ void q8ref_pack(const uint8_t *blocks, int64_t N, int64_t K, uint8_t *packed)
             }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Gated feed-forward step after the gate and up products (the step after   */
+/* the path; the pages' engine runs Qwen3.5/3.6 models, whose FFNs are      */
+/* gated; the pages do not spell the FFN out, so this is the plainest       */
+/* reading): h = silu(g) * u with silu(x) = x / (1 + e^-x), then each row   */
+/* of h quantised to Q8_0 blocks of 32 along the hidden dimension -- the    */
+/* activation format the down projection consumes.                          */
+/* ------------------------------------------------------------------------ */
+
+double q8ref_silu(double x)
+{
+    return x / (1.0 + exp(-x));
+}
+
+/* G, U: [M][I] doubles (the gate and up products, e.g. from q8ref_gemm).
+ * h: [M][I] doubles out (may be NULL).  q [M][I] int8 and d [M][I/32]
+ * binary16 out: h rounded to binary32, then quantised block by block
+ * (q8ref_quantize_block).  I % 32 == 0. */
+void q8ref_swiglu_quant(int64_t M, int64_t I, const double *G, const double *U,
+                        double *h, int8_t *q, uint16_t *d)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t b = 0; b < I / QK; ++b) {
+            float x[QK];
+            for (int j = 0; j < QK; ++j) {
+                int64_t i = m * I + b * QK + j;
+                double v = q8ref_silu(G[i]) * U[i];
+                if (h) h[i] = v;
+                x[j] = (float)v;
+            }
+            q8ref_quantize_block(x, q + m * I + b * QK, d + m * (I / QK) + b);
+        }
+}
+
 /* Threads the OpenMP runtime will use (for reporting the CPU baseline). */
 int q8ref_num_threads(void)
 {

@@ -340,7 +340,102 @@ def pin_pack_layout(orc):
     assert sorted(qp[qp != 0].tolist()) == sorted(q[q != 0].tolist())
 
 
+# --------------------------------------------------------------------------
+# gated FFN step: h = silu(g) * u, quantised per 32 along the hidden dimension
+# --------------------------------------------------------------------------
+
+def pin_silu(orc):
+    """silu(x) = x / (1 + e^-x), checked through properties and other
+    formulas: silu(x) - silu(-x) = x exactly in the reals; silu(x) =
+    x (1 + tanh(x/2)) / 2 for x >= 0 and x e^x / (1 + e^x) for x < 0 (both
+    free of cancellation there); silu(0) = 0; silu(x) = x where e^-x
+    vanishes against 1 in double; silu -> -0 where e^-x overflows."""
+    assert orc.silu(0.0) == 0.0
+    r = np.random.default_rng(31)
+    xs = np.concatenate([np.linspace(-30, 30, 601), r.standard_normal(500) * 8])
+    for x in xs:
+        x = float(x)
+        a, b = orc.silu(x), orc.silu(-x)
+        assert abs((a - b) - x) <= 4e-16 * max(1.0, abs(x)), x
+        if x >= 0:
+            ref = x * (1.0 + np.tanh(x / 2.0)) / 2.0
+        else:
+            ref = x * np.exp(x) / (1.0 + np.exp(x))
+        assert abs(a - ref) <= 1e-15 * max(abs(ref), 1e-300) + 1e-300, (x, a, ref)
+    assert orc.silu(50.0) == 50.0 and orc.silu(64.0) == 64.0
+    assert orc.silu(-800.0) == 0.0
+
+
+def pin_swiglu_golden(orc):
+    """Hand-derived blocks.  Block 0: g = 64 (silu(64) = 64 in double) and
+    u = t/64 with integers t in [-127, 127] that reach +-127, so h = t
+    exactly, d32 = 1, q = t, d = binary16(1) = 0x3C00.  Block 1: g = -800
+    (silu = -0), so h = 0, q = 0, d = 0.  Block 2: h = t + 1/2 for t < 127
+    next to an element 127, so d32 = 1 and the halves round away from zero."""
+    r = np.random.default_rng(32)
+    t = r.integers(-126, 127, 32)
+    t[5], t[20] = 127, -127
+    t2 = r.integers(-120, 120, 32)
+    half = t2 + 0.5
+    half[0] = 127.0
+    G = np.concatenate([np.full(32, 64.0), np.full(32, -800.0), np.full(32, 64.0)])[None, :]
+    U = np.concatenate([t / 64.0, r.standard_normal(32), half / 64.0])[None, :]
+    h, q, d = orc.swiglu_quant(G, U)
+    assert np.array_equal(h[0, :32], t.astype(np.float64))
+    assert np.array_equal(q[0, :32], t.astype(np.int8)) and d[0, 0] == 0x3C00
+    assert not np.any(q[0, 32:64]) and d[0, 1] == 0
+    want = np.where(half >= 0, np.floor(half) + 1, -(np.floor(-half) + 1))
+    want[0] = 127
+    assert np.array_equal(q[0, 64:96], want.astype(np.int8)) and d[0, 2] == 0x3C00
+
+
+def pin_swiglu_rows(orc):
+    """Random gate/up products: h equals silu (tanh form) times u, and q, d
+    are the pinned quantiser applied to h rounded to binary32."""
+    r = np.random.default_rng(33)
+    M, I = 3, 160
+    G = r.standard_normal((M, I)) * 3.0
+    U = r.standard_normal((M, I)) * 2.0
+    h, q, d = orc.swiglu_quant(G, U)
+    sig = np.where(G >= 0, (1.0 + np.tanh(G / 2.0)) / 2.0, np.exp(G) / (1.0 + np.exp(G)))
+    ref = G * sig * U
+    assert np.all(np.abs(h - ref) <= 1e-14 * np.maximum(np.abs(ref), 1e-300))
+    q2, d2 = orc.quantize_rows(h.astype(np.float32))
+    assert np.array_equal(q, q2) and np.array_equal(d, d2)
+
+
+def pin_gateup_layout(orc):
+    """The gate/up interleave, by brute force from its description: 64-row
+    group g of the packed weight holds gate rows 32g..32g+31, then up rows
+    32g..32g+31; and the packed bytes are the pack of those rows."""
+    I, K = 96, 64
+    r = np.random.default_rng(34)
+    gate = r.integers(0, 256, (I, 5)).astype(np.uint8)
+    up = r.integers(0, 256, (I, 5)).astype(np.uint8)
+    rows = orc.interleave_gateup(gate, up)
+    assert rows.shape == (2 * I, 5)
+    for n in range(2 * I):
+        g, rr = divmod(n, 64)
+        src = gate[32 * g + rr] if rr < 32 else up[32 * g + rr - 32]
+        assert np.array_equal(rows[n], src), n
+    qg = r.integers(-127, 128, (I, K)).astype(np.int8)
+    qu = r.integers(-127, 128, (I, K)).astype(np.int8)
+    dg = r.integers(1, 0x7BFF, (I, K // 32)).astype(np.uint16)
+    du = r.integers(1, 0x7BFF, (I, K // 32)).astype(np.uint16)
+    packed = orc.pack_gateup(orc.blocks_from_qd(qg, dg), orc.blocks_from_qd(qu, du), I, K)
+    KB, NG = K // 32, 2 * I // 64
+    qp = packed[:NG * KB * 2048].view(np.int8)
+    sp = packed[NG * KB * 2048:].view(np.uint16)
+    for (g, kb, h_, rr, t_) in [(0, 0, 0, 0, 0), (0, 1, 1, 31, 15), (1, 0, 1, 32, 3), (2, 1, 0, 63, 9)]:
+        srcq = qg if rr < 32 else qu
+        assert qp[((g * KB + kb) * 2 + h_) * 1024 + rr * 16 + t_] == \
+            srcq[32 * g + rr % 32, 32 * kb + 16 * h_ + t_]
+    for (g, kb, rr) in [(0, 0, 3), (1, 1, 40), (2, 0, 33)]:
+        srcd = dg if rr < 32 else du
+        assert sp[(g * KB + kb) * 64 + rr] == srcd[32 * g + rr % 32, kb]
+
+
 ALL_PINS = [pin_f16_roundtrip_all, pin_f16_vs_numpy, pin_quant_golden, pin_quant_exact_random,
             pin_quant_invariants, pin_quant_rows, pin_gemm_golden, pin_gemm_exact,
             pin_gemm_unit_scale, pin_block_dots, pin_gemm_sampled, pin_block_bytes,
-            pin_pack_layout]
+            pin_pack_layout, pin_silu, pin_swiglu_golden, pin_swiglu_rows, pin_gateup_layout]

@@ -37,6 +37,10 @@ MUTANTS = {
     "pack_half_order": ("b ? b[2 + 16 * h + t] : 0;", "b ? b[2 + 16 * (1 - h) + t] : 0;"),
     "sampled_wrong_row": ("one_output(q_a + rows[i] * K, d_a + rows[i] * KB,",
                           "one_output(q_a + cols[i] * K, d_a + rows[i] * KB,"),
+    "swiglu_gate_up_swapped": ("double v = q8ref_silu(G[i]) * U[i];",
+                               "double v = q8ref_silu(U[i]) * G[i];"),
+    "silu_sign": ("return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
+    "swiglu_scale_index": ("d + m * (I / QK) + b);", "d + b * M + m);"),
 }
 
 
@@ -59,3 +63,18 @@ def test_mutant_fails_a_pin(name, tmp_path):
         except Exception as e:          # a crash or a shape error also counts
             failed.append("%s (%s)" % (pin.__name__, type(e).__name__))
     assert failed, "planted mistake %r passed every pin" % name
+
+
+def test_wrong_gateup_interleave_fails_its_pin():
+    """The gate/up interleave lives in the oracle's Python layer: a copy with
+    the halves of each group swapped must fail pin_gateup_layout."""
+    orc = oracle.default()
+
+    class Swapped(oracle.Oracle):
+        @staticmethod
+        def interleave_gateup(gate_rows, up_rows):
+            return oracle.Oracle.interleave_gateup(up_rows, gate_rows)
+
+    bad = Swapped(orc.path)
+    with pytest.raises(AssertionError):
+        pins.pin_gateup_layout(bad)
