@@ -162,6 +162,55 @@ q8_status q8_gemm_act(const void *x, q8_dtype dtype, int64_t M, int64_t N, int64
                       int64_t ldx, const void *w_packed, float *C, int64_t ldc,
                       int8_t *q_a, uint16_t *d_a, void *stream);
 
+/*
+ * q8_pack_weights_gateup -- pack the gate and up weights of a gated
+ * feed-forward layer together, for q8_gemm_swiglu.
+ *
+ * Operation: a byte permutation, as q8_pack_weights, of the 2I rows
+ * obtained by interleaving the two weights by 32-row blocks: packed row
+ * 64g + r is gate row 32g + r for r < 32 and up row 32g + r - 32 for
+ * r >= 32.  The result is the packed layout (see q8_pack_weights) of that
+ * 2I x K matrix, so the gate and the up rows of a hidden unit share a row
+ * group.  (The step after the product in the source engine's Qwen3.5/3.6
+ * layers: their feed-forward blocks are gated; see the note at the top.)
+ *
+ * w_gate, w_up  [I][K/32] GGUF Q8_0 blocks of 34 bytes each (as w_blocks).
+ * I     hidden units; I >= 32, I % 32 == 0.  K as for q8_pack_weights.
+ * w_packed, packed_bytes  as for q8_pack_weights with N = 2I.
+ *
+ * Errors: Q8_ERR_NULL, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_SIZE,
+ * Q8_ERR_DEVICE, Q8_ERR_LAUNCH.
+ */
+q8_status q8_pack_weights_gateup(const void *w_gate, const void *w_up, int64_t I, int64_t K,
+                                 void *w_packed, size_t *packed_bytes, void *stream);
+
+/*
+ * q8_gemm_swiglu -- gate and up products, the gated activation and its
+ * quantisation for the down projection, in one call:
+ *
+ *     g = A * Wg^T,  u = A * Wu^T       (each as q8_gemm, binary32)
+ *     h = silu(g) * u,  silu(x) = x / (1 + e^-x)     (binary32)
+ *     (q_h, d_h) = Q8_0 quantisation of the rows of h (as q8_quantize_act)
+ *
+ * g and u never go through memory: the matrix-core kernel (M > 8) and the
+ * decode kernel (M <= 8) apply the step to their accumulators.  Precision:
+ * g and u carry the bound of q8_gemm; silu uses the device's binary32 exp
+ * and a correctly rounded division, and the product is rounded once; the
+ * codes are then decided in binary32 like q8_quantize_act.  A value of h
+ * within a few binary32 units of a rounding boundary of the quantiser may
+ * therefore land on either side of it.
+ *
+ * q_a, d_a  the quantised activations [M][K] (as for q8_gemm).
+ * w_packed  the output of q8_pack_weights_gateup for the same I and K.
+ * q_h   [M][I] int8 out; d_h [M][I/32] binary16 out (2-byte aligned).
+ *
+ * Errors: Q8_ERR_NULL, Q8_ERR_SHAPE (I < 32 or I % 32 != 0, bad K or M),
+ * Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH.
+ */
+q8_status q8_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t *q_a,
+                         const uint16_t *d_a, const void *w_packed, int8_t *q_h,
+                         uint16_t *d_h, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *q8_status_string(q8_status s);
 

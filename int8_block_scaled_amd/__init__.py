@@ -11,6 +11,8 @@ The calls keep the C names:
 * ``q8_quantize_act(x, K=None)``       fp32/bf16 rows -> (int8 q, fp16 d)
 * ``q8_gemm(q_a, d_a, w_packed, N, K)``  C = A W^T in fp32
 * ``q8_gemm_act(x, w_packed, N, K)``  quantise x on the fly, then C = A W^T
+* ``q8_pack_weights_gateup(w_gate, w_up, I, K)``  gate and up weights packed together
+* ``q8_gemm_swiglu(q_a, d_a, w_packed, I, K)``  Q8_0(silu(A Wg^T) * (A Wu^T))
 """
 import ctypes
 import functools
@@ -24,7 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libq8gemm.so")
 Q8_F32, Q8_BF16 = 0, 1
 STATUS = {0: "Q8_OK", 1: "Q8_ERR_NULL", 2: "Q8_ERR_SHAPE", 3: "Q8_ERR_ALIGN",
           4: "Q8_ERR_DTYPE", 5: "Q8_ERR_SIZE", 6: "Q8_ERR_DEVICE", 7: "Q8_ERR_LAUNCH"}
-EXPORTS = ("q8_pack_weights", "q8_quantize_act", "q8_gemm", "q8_gemm_act", "q8_status_string")
+EXPORTS = ("q8_pack_weights", "q8_quantize_act", "q8_gemm", "q8_gemm_act",
+           "q8_pack_weights_gateup", "q8_gemm_swiglu", "q8_status_string")
 
 _lib = None
 
@@ -54,6 +57,10 @@ def _load():
         L.q8_gemm.restype = ctypes.c_int
         L.q8_gemm_act.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, i64, vp, vp, vp]
         L.q8_gemm_act.restype = ctypes.c_int
+        L.q8_pack_weights_gateup.argtypes = [vp, vp, i64, i64, vp, ctypes.POINTER(sz), vp]
+        L.q8_pack_weights_gateup.restype = ctypes.c_int
+        L.q8_gemm_swiglu.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.q8_gemm_swiglu.restype = ctypes.c_int
         L.q8_status_string.argtypes = [ctypes.c_int]
         L.q8_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -191,3 +198,59 @@ def q8_gemm_act(x: torch.Tensor, w_packed: torch.Tensor, N: int, K: int = None,
     _check("q8_gemm_act", _load().q8_gemm_act(_ptr(x), dt, M, N, K, ldx, _ptr(w_packed),
                                               _ptr(out), ldc, qp, dp, _stream(x)))
     return out
+
+
+@functools.lru_cache(maxsize=256)
+def q8_packed_bytes_gateup(I: int, K: int) -> int:
+    """Size of the packed gate/up weight for I hidden units."""
+    n = ctypes.c_size_t(0)
+    _check("q8_pack_weights_gateup",
+           _load().q8_pack_weights_gateup(None, None, I, K, None, ctypes.byref(n), None))
+    return n.value
+
+
+def q8_pack_weights_gateup(w_gate: torch.Tensor, w_up: torch.Tensor, I: int, K: int,
+                           out: torch.Tensor = None) -> torch.Tensor:
+    """GGUF Q8_0 blocks of the gate and up weights (uint8, I*K/32*34 bytes
+    each, on the GPU) -> one packed uint8 buffer for q8_gemm_swiglu."""
+    for name, t in (("w_gate", w_gate), ("w_up", w_up)):
+        _need_cuda(name, t)
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise TypeError("%s must be contiguous uint8" % name)
+        if t.numel() != I * (K // 32) * 34:
+            raise ValueError("%s holds %d bytes, expected I*K/32*34 = %d"
+                             % (name, t.numel(), I * (K // 32) * 34))
+    need = q8_packed_bytes_gateup(I, K)
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=w_gate.device)
+    n = ctypes.c_size_t(out.numel())
+    _check("q8_pack_weights_gateup", _load().q8_pack_weights_gateup(
+        _ptr(w_gate), _ptr(w_up), I, K, _ptr(out), ctypes.byref(n), _stream(w_gate)))
+    return out
+
+
+def q8_gemm_swiglu(q_a: torch.Tensor, d_a: torch.Tensor, w_packed: torch.Tensor, I: int, K: int,
+                   q: torch.Tensor = None, d: torch.Tensor = None):
+    """(q_h int8 [M][I], d_h float16 [M][I/32]) = Q8_0 of silu(A Wg^T) * (A Wu^T)."""
+    for name, t in (("q_a", q_a), ("d_a", d_a), ("w_packed", w_packed)):
+        _need_cuda(name, t)
+    if q_a.dtype != torch.int8 or not q_a.is_contiguous() or q_a.dim() != 2 or q_a.shape[1] != K:
+        raise TypeError("q_a must be contiguous int8 [M][K]")
+    if d_a.dtype not in (torch.float16, torch.int16) or not d_a.is_contiguous() \
+            or tuple(d_a.shape) != (q_a.shape[0], K // 32):
+        raise TypeError("d_a must be contiguous float16 [M][K/32]")
+    if w_packed.numel() < q8_packed_bytes_gateup(I, K):
+        raise ValueError("w_packed is smaller than the gate/up packed layout for I=%d K=%d" % (I, K))
+    M = q_a.shape[0]
+    if q is None:
+        q = torch.empty((M, I), dtype=torch.int8, device=q_a.device)
+    if d is None:
+        d = torch.empty((M, I // 32), dtype=torch.float16, device=q_a.device)
+    if q.dtype != torch.int8 or not q.is_contiguous() or tuple(q.shape) != (M, I):
+        raise TypeError("q must be contiguous int8 [M][I]")
+    if d.dtype not in (torch.float16, torch.int16) or not d.is_contiguous() \
+            or tuple(d.shape) != (M, I // 32):
+        raise TypeError("d must be contiguous float16 [M][I/32]")
+    _check("q8_gemm_swiglu", _load().q8_gemm_swiglu(M, I, K, _ptr(q_a), _ptr(d_a), _ptr(w_packed),
+                                                    _ptr(q), _ptr(d), _stream(q_a)))
+    return q, d

@@ -118,6 +118,51 @@ q8_status q8_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint
   return e == hipSuccess ? Q8_OK : Q8_ERR_LAUNCH;
 }
 
+q8_status q8_pack_weights_gateup(const void* w_gate, const void* w_up, int64_t I, int64_t K,
+                                 void* w_packed, size_t* packed_bytes, void* stream) {
+  if (packed_bytes == nullptr) return Q8_ERR_NULL;
+  if (I < 32 || I % 32 != 0 || 2 * I >= kMaxDim || !valid_k(K)) return Q8_ERR_SHAPE;
+  const int64_t NG = q8::num_groups(2 * I);
+  const int64_t KB = K / q8::kQK;
+  const size_t need = static_cast<size_t>(NG * KB) * (q8::kGroupBlockBytes + 2 * q8::kGroupRows);
+  if (w_packed == nullptr) {
+    *packed_bytes = need;
+    return Q8_OK;
+  }
+  if (w_gate == nullptr || w_up == nullptr) return Q8_ERR_NULL;
+  if (!aligned(w_packed, 16)) return Q8_ERR_ALIGN;
+  if (*packed_bytes < need) return Q8_ERR_SIZE;
+  if (NG * KB * 2 * q8::kGroupRows / 256 >= kMaxDim) return Q8_ERR_SHAPE;
+  const q8_status dev = check_device();
+  if (dev != Q8_OK) return dev;
+  return q8::launch_pack_gateup(static_cast<const uint8_t*>(w_gate),
+                                static_cast<const uint8_t*>(w_up), I, K,
+                                static_cast<uint8_t*>(w_packed), as_stream(stream)) == hipSuccess
+             ? Q8_OK
+             : Q8_ERR_LAUNCH;
+}
+
+q8_status q8_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a, const uint16_t* d_a,
+                         const void* w_packed, int8_t* q_h, uint16_t* d_h, void* stream) {
+  if (M < 0 || I < 32 || I % 32 != 0 || 2 * I >= kMaxDim || !valid_k(K)) return Q8_ERR_SHAPE;
+  if (M == 0) return Q8_OK;
+  if (q_a == nullptr || d_a == nullptr || w_packed == nullptr || q_h == nullptr ||
+      d_h == nullptr)
+    return Q8_ERR_NULL;
+  if (!aligned(q_a, 16) || !aligned(d_a, 2) || !aligned(w_packed, 16) || !aligned(d_h, 2))
+    return Q8_ERR_ALIGN;
+  if (((M + 127) / 128) * ((2 * I + 127) / 128) >= kMaxDim) return Q8_ERR_SHAPE;
+  const q8_status dev = check_device();
+  if (dev != Q8_OK) return dev;
+  const uint8_t* wp = static_cast<const uint8_t*>(w_packed);
+  const hipError_t e =
+      M <= q8::kGemvMaxM
+          ? q8::launch_gemv_swiglu(static_cast<int>(M), I, K, q_a, d_a, wp, q_h, d_h,
+                                   as_stream(stream))
+          : q8::launch_gemm_swiglu(M, I, K, q_a, d_a, wp, q_h, d_h, as_stream(stream));
+  return e == hipSuccess ? Q8_OK : Q8_ERR_LAUNCH;
+}
+
 q8_status q8_gemm_act(const void* x, q8_dtype dtype, int64_t M, int64_t N, int64_t K,
                       int64_t ldx, const void* w_packed, float* C, int64_t ldc, int8_t* q_a,
                       uint16_t* d_a, void* stream) {

@@ -452,12 +452,16 @@ __device__ __forceinline__ void compute_stage16(uint32_t base_a, uint32_t base_a
   });
 }
 
-template <class T, int kWavesPerEU>
+// kSwiglu: the weight is a gate/up-packed weight (64-row group g = gate
+// rows 32g.., then up rows 32g..; N = 2I) and, instead of C, the kernel
+// writes h = silu(gate) * up quantised to Q8_0: q_h [M][I], d_h [M][I/32].
+template <class T, int kWavesPerEU, bool kSwiglu = false>
 __global__ __launch_bounds__(T::kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restrict__ d_a,
                          const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
                          float* __restrict__ C, int64_t M, int64_t N, int64_t K, int64_t KB,
-                         int64_t NG, int64_t ldc, int tiles_m, int remap) {
+                         int64_t NG, int64_t ldc, int tiles_m, int remap,
+                         int8_t* __restrict__ q_h, uint16_t* __restrict__ d_h) {
   constexpr int TM = T::TM, TN = T::TN, BM = T::BM, BN = T::BN, KBS = T::KBS;
   __shared__ __align__(16) uint8_t smem[T::NBUF * T::kStage];
   const int tid = threadIdx.x;
@@ -565,6 +569,30 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   }
   wait_vmcnt<0>();   // the loads issued past the end are done before LDS is released
 
+  if constexpr (kSwiglu) {
+    // The wave's 64 columns are one row group: column l32 is the gate of
+    // hidden unit 32*grp + l32 and column 32 + l32 its up, both in this lane
+    // (j = 0 and 1); a half-wave's 32 lanes hold one 32-unit block of a row.
+    static_assert(T::MF == 32 && T::TN == 2, "one 64-column row group per wave");
+    const int64_t grp = (n0 + wn0) / kGroupRows;
+    if (n0 + wn0 < N) {
+      const int64_t I = N / 2;
+      const int64_t hid = grp * 32 + l32;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+          uint16_t dbits;
+          const int q = quantize_lane32(silu_mul(acc[i][0][r], acc[i][1][r]), dbits);
+          if (row < M) {
+            q_h[row * I + hid] = static_cast<int8_t>(q);
+            if (l32 == 0) d_h[row * (I / kQK) + grp] = dbits;
+          }
+        }
+    }
+    return;
+  }
   // Output.  32x32: lane holds column wn0 + 32j + l32 and rows
   // 8*(r/4) + 4*half + r%4; 16x16: column wn0 + 16j + l16, rows 4*g + r.
 #pragma unroll
@@ -582,9 +610,10 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   }
 }
 
-template <class T, int kOcc>
-hipError_t launch_tile(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
-                       const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
+template <class T, int kOcc, bool kSwiglu>
+hipError_t launch_tile_impl(int64_t M, int64_t N, int64_t K, const int8_t* q_a,
+                            const uint16_t* d_a, const uint8_t* w_packed, float* C, int64_t ldc,
+                            hipStream_t stream, int8_t* q_h, uint16_t* d_h) {
   const int64_t KB = K / kQK;
   const int64_t NG = num_groups(N);
   const uint16_t* ws = reinterpret_cast<const uint16_t*>(w_packed + NG * KB * kGroupBlockBytes);
@@ -592,10 +621,17 @@ hipError_t launch_tile(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const
   const int64_t tiles_n = (N + T::BN - 1) / T::BN;
   const int64_t grid = tiles_m * tiles_n;
   const int remap = (grid % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((gemm_q8_mfma_kernel<T, kOcc>), dim3(static_cast<uint32_t>(grid)),
+  hipLaunchKernelGGL((gemm_q8_mfma_kernel<T, kOcc, kSwiglu>), dim3(static_cast<uint32_t>(grid)),
                      dim3(T::kThreads), 0, stream, q_a, d_a, w_packed, ws, C, M, N, K, KB, NG,
-                     ldc, static_cast<int>(tiles_m), remap);
+                     ldc, static_cast<int>(tiles_m), remap, q_h, d_h);
   return hipGetLastError();
+}
+
+template <class T, int kOcc>
+hipError_t launch_tile(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
+                       const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
+  return launch_tile_impl<T, kOcc, false>(M, N, K, q_a, d_a, w_packed, C, ldc, stream, nullptr,
+                                          nullptr);
 }
 
 typedef hipError_t (*launcher_t)(int64_t, int64_t, int64_t, const int8_t*, const uint16_t*,
@@ -633,6 +669,25 @@ int pick_tile(int64_t M, int64_t N) {
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                        const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
   return kTiles[pick_tile(M, N)].launch(M, N, K, q_a, d_a, w_packed, C, ldc, stream);
+}
+
+hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a,
+                              const uint16_t* d_a, const uint8_t* w_packed, int8_t* q_h,
+                              uint16_t* d_h, hipStream_t stream) {
+  // The 32x32-MFMA tiles with 64-column wave tiles (0, 1 and 3) carry the
+  // epilogue; the 16x16 variant (2) is replaced by tile 0.
+  const int64_t N = 2 * I;
+  switch (pick_tile(M, N)) {
+    case 1:
+      return launch_tile_impl<Tile<64, 128, 2, 2, 2, 2>, 4, true>(M, N, K, q_a, d_a, w_packed,
+                                                                  nullptr, N, stream, q_h, d_h);
+    case 3:
+      return launch_tile_impl<Tile<128, 256, 4, 4, 4, 2>, 4, true>(M, N, K, q_a, d_a, w_packed,
+                                                                   nullptr, N, stream, q_h, d_h);
+    default:
+      return launch_tile_impl<Tile<128, 128, 4, 2, 4, 2>, 4, true>(M, N, K, q_a, d_a, w_packed,
+                                                                   nullptr, N, stream, q_h, d_h);
+  }
 }
 
 }  // namespace q8

@@ -42,11 +42,17 @@ constexpr int kThreads = kMaxWaves * 64;
 // Block indices past the wave's range are clamped to its last block (a
 // cached re-read) and their contribution is dropped, so the code is
 // straight-line and every load of the chunk is in flight together.
-template <int MR, int L, bool NT>
+//
+// kSwiglu: the weight is gate/up-packed (64-row group g = gate rows 32g..,
+// then up rows 32g..; N = 2I): row r and row r + 32 of the group are the
+// gate and up of hidden unit 32g + r, so instead of C the workgroup writes
+// the Q8_0 block g of h = silu(gate) * up: q_h [M][I], d_h [M][I/32].
+template <int MR, int L, bool NT, bool kSwiglu = false>
 __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(
     const int8_t* __restrict__ q_a, const uint16_t* __restrict__ d_a,
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
-    float* __restrict__ C, int64_t N, int64_t K, int64_t KB, int64_t ldc, int kb_per_wave) {
+    float* __restrict__ C, int64_t N, int64_t K, int64_t KB, int64_t ldc, int kb_per_wave,
+    int8_t* __restrict__ q_h = nullptr, uint16_t* __restrict__ d_h = nullptr) {
   __shared__ float red[kMaxWaves][MR][64];
   const int64_t g = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -102,6 +108,24 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_kernel(
 #pragma unroll
   for (int m = 0; m < MR; ++m) red[wave][m][lane] = acc[m];
   __syncthreads();
+  if constexpr (kSwiglu) {
+    // MR*32 hidden units; each 32 consecutive threads (32-aligned lanes of
+    // one wave, since blockDim is a multiple of 64) hold one block.
+    const int64_t I = N / 2;
+    for (int t = threadIdx.x; t < MR * 32; t += blockDim.x) {
+      const int m = t >> 5, r = t & 31;
+      float gsum = 0.0f, usum = 0.0f;
+      for (int w = 0; w < nwaves; ++w) {
+        gsum += red[w][m][r];
+        usum += red[w][m][r + 32];
+      }
+      uint16_t dbits;
+      const int q = quantize_lane32(silu_mul(gsum, usum), dbits);
+      q_h[m * I + g * 32 + r] = static_cast<int8_t>(q);
+      if (r == 0) d_h[m * (I / kQK) + g] = dbits;
+    }
+    return;
+  }
   // MR*64 sums; a workgroup may have fewer than MR waves when KB is small.
   for (int t = threadIdx.x; t < MR * 64; t += blockDim.x) {
     const int m = t >> 6, r = t & 63;
@@ -334,17 +358,18 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_act_kernel(
   }
 }
 
-template <int MR, int L, bool NT>
+template <int MR, int L, bool NT, bool kSwiglu = false>
 hipError_t launch_m(int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                     const uint8_t* w_packed, float* C, int64_t ldc, int max_waves,
-                    hipStream_t stream) {
+                    hipStream_t stream, int8_t* q_h = nullptr, uint16_t* d_h = nullptr) {
   const int64_t KB = K / kQK;
   const int64_t NG = num_groups(N);
   const int waves = static_cast<int>(KB < max_waves ? KB : max_waves);
   const int kb_per_wave = static_cast<int>((KB + waves - 1) / waves);
   const uint16_t* ws = reinterpret_cast<const uint16_t*>(w_packed + NG * KB * kGroupBlockBytes);
-  hipLaunchKernelGGL((gemv_q8_kernel<MR, L, NT>), dim3(static_cast<uint32_t>(NG)), dim3(waves * 64),
-                     0, stream, q_a, d_a, w_packed, ws, C, N, K, KB, ldc, kb_per_wave);
+  hipLaunchKernelGGL((gemv_q8_kernel<MR, L, NT, kSwiglu>), dim3(static_cast<uint32_t>(NG)),
+                     dim3(waves * 64), 0, stream, q_a, d_a, w_packed, ws, C, N, K, KB, ldc,
+                     kb_per_wave, q_h, d_h);
   return hipGetLastError();
 }
 
@@ -391,6 +416,28 @@ hipError_t launch_act_m(const void* x, bool bf16, int64_t ldx, int64_t N, int64_
 }
 
 }  // namespace
+
+hipError_t launch_gemv_swiglu(int M, int64_t I, int64_t K, const int8_t* q_a,
+                              const uint16_t* d_a, const uint8_t* w_packed, int8_t* q_h,
+                              uint16_t* d_h, hipStream_t stream) {
+  const int64_t N = 2 * I;
+#define Q8_SWIGLU_M(MR)                                                                     \
+  case MR:                                                                                  \
+    return launch_m<MR, 4, true, true>(N, K, q_a, d_a, w_packed, nullptr, 0, 16, stream, q_h, \
+                                       d_h);
+  switch (M) {
+    Q8_SWIGLU_M(1)
+    Q8_SWIGLU_M(2)
+    Q8_SWIGLU_M(3)
+    Q8_SWIGLU_M(4)
+    Q8_SWIGLU_M(5)
+    Q8_SWIGLU_M(6)
+    Q8_SWIGLU_M(7)
+    Q8_SWIGLU_M(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef Q8_SWIGLU_M
+}
 
 hipError_t launch_gemv_act(int M, const void* x, int dtype, int64_t ldx, int64_t N, int64_t K,
                            const uint8_t* w_packed, float* C, int64_t ldc, int8_t* q_out,

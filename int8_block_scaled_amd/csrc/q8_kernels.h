@@ -24,6 +24,17 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t M, int64_t K, int64
                            int8_t* q, uint16_t* d, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* blocks, int64_t N, int64_t K, uint8_t* packed,
                        hipStream_t stream);
+// Gate and up weights ([I][K/32] blocks each) packed as their 2I interleaved
+// rows: 64-row group g = gate rows 32g..32g+31, then up rows 32g..32g+31.
+hipError_t launch_pack_gateup(const uint8_t* gate, const uint8_t* up, int64_t I, int64_t K,
+                              uint8_t* packed, hipStream_t stream);
+// Gated FFN step on gate/up-packed weights: q_h/d_h = Q8_0(silu(A Wg^T) * (A Wu^T)).
+hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a,
+                              const uint16_t* d_a, const uint8_t* w_packed, int8_t* q_h,
+                              uint16_t* d_h, hipStream_t stream);
+hipError_t launch_gemv_swiglu(int M, int64_t I, int64_t K, const int8_t* q_a,
+                              const uint16_t* d_a, const uint8_t* w_packed, int8_t* q_h,
+                              uint16_t* d_h, hipStream_t stream);
 hipError_t launch_gemv(int M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                        const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream);
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
@@ -81,10 +92,29 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t off, f
   }
 }
 
+// A block's scale from its maximum magnitude: d32 = amax/127; id = 1/d32
+// and the binary16 bits of d32.  Returns false (codes 0, d = +0) when
+// d32 < FLT_MIN (an all-zero block, or a binary32-subnormal scale).
+__device__ __forceinline__ bool block_scale(float amax, float& id, uint16_t& dbits) {
+  const float d32 = amax / 127.0f;
+  if (!(d32 >= 1.17549435e-38f)) {   // FLT_MIN
+    id = 0.0f;
+    dbits = 0;
+    return false;
+  }
+  id = 1.0f / d32;
+  dbits = f32_to_f16_bits(d32);
+  return true;
+}
+
+// A value's code: v * id rounded half away from zero (|code| <= 127).
+__device__ __forceinline__ int block_code(float v, float id) {
+  return static_cast<int>(roundf(v * id));
+}
+
 // Quantise the lane's eight values of a block: codes packed little-endian
 // into lo (values 0..3) and hi (4..7), and the block's binary16 scale bits.
-// Blocks with d32 < FLT_MIN (all zero, or a binary32-subnormal scale) give
-// zero codes and d = +0.  All four lanes of every block must be active.
+// All four lanes of every block must be active.
 __device__ __forceinline__ void quantize8(const float v[8], uint32_t& lo, uint32_t& hi,
                                           uint16_t& dbits) {
   float amax = 0.0f;
@@ -92,22 +122,37 @@ __device__ __forceinline__ void quantize8(const float v[8], uint32_t& lo, uint32
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 1, 4));
   amax = fmaxf(amax, __shfl_xor(amax, 2, 4));
-  const float d32 = amax / 127.0f;
+  float id;
   lo = 0;
   hi = 0;
-  dbits = 0;
-  if (d32 >= 1.17549435e-38f) {   // FLT_MIN
-    const float id = 1.0f / d32;
+  if (block_scale(amax, id, dbits)) {
     uint32_t b[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int qi = static_cast<int>(roundf(v[i] * id));  // |qi| <= 127
-      b[i] = static_cast<uint32_t>(qi) & 0xffu;
-    }
+    for (int i = 0; i < 8; ++i) b[i] = static_cast<uint32_t>(block_code(v[i], id)) & 0xffu;
     lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
     hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-    dbits = f32_to_f16_bits(d32);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Gated feed-forward step applied to the gate and up products g, u of one
+// hidden unit: h = silu(g) * u, silu(x) = x / (1 + e^-x), in binary32
+// (device expf, correctly rounded division, one rounding for the product);
+// then h is quantised like an activation, in blocks of 32 hidden units that
+// sit in 32 consecutive, 32-aligned lanes of a wave (one value each).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
+// Every lane of the 32-lane group must take part (lane exchanges).  Returns
+// the lane's code; dbits receives the block's scale bits.
+__device__ __forceinline__ int quantize_lane32(float h, uint16_t& dbits) {
+  float amax = fabsf(h);
+#pragma unroll
+  for (int s = 16; s >= 1; s >>= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 32));
+  float id;
+  return block_scale(amax, id, dbits) ? block_code(h, id) : 0;
 }
 
 }  // namespace q8

@@ -115,6 +115,40 @@ def test_gemm_act_validation(L):
     assert f(FAKE, 0, 4, 64, 64, 64, FAKE, FAKE, 64, FAKE, ODD, None) == ALIGN
 
 
+def test_gateup_pack_validation(L, orc):
+    n = ctypes.c_size_t(0)
+    assert L.q8_pack_weights_gateup(None, None, 64, 512, None, ctypes.byref(n), None) == OK
+    assert n.value == orc.packed_bytes(128, 512) == q8.q8_packed_bytes_gateup(64, 512)
+    big = ctypes.c_size_t(1 << 40)
+    assert L.q8_pack_weights_gateup(FAKE, FAKE, 64, 512, FAKE, None, None) == NULL
+    assert L.q8_pack_weights_gateup(FAKE, FAKE, 48, 512, FAKE, ctypes.byref(big), None) == SHAPE
+    assert L.q8_pack_weights_gateup(FAKE, FAKE, 0, 512, FAKE, ctypes.byref(big), None) == SHAPE
+    assert L.q8_pack_weights_gateup(FAKE, FAKE, 64, 48, FAKE, ctypes.byref(big), None) == SHAPE
+    assert L.q8_pack_weights_gateup(None, FAKE, 64, 512, FAKE, ctypes.byref(big), None) == NULL
+    assert L.q8_pack_weights_gateup(FAKE, None, 64, 512, FAKE, ctypes.byref(big), None) == NULL
+    assert L.q8_pack_weights_gateup(FAKE, FAKE, 64, 512, ODD, ctypes.byref(big), None) == ALIGN
+    small = ctypes.c_size_t(100)
+    assert L.q8_pack_weights_gateup(FAKE, FAKE, 64, 512, FAKE, ctypes.byref(small), None) == SIZE
+
+
+def test_gemm_swiglu_validation(L):
+    f = L.q8_gemm_swiglu
+    #        M   I   K    qa    da    w     qh    dh
+    assert f(-1, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(4, 48, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(4, 16, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(4, 64, 65, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(0, 64, 64, None, None, None, None, None, None) == OK      # M == 0: no-op
+    for i in range(5):
+        args = [FAKE] * 5
+        args[i] = None
+        assert f(4, 64, 64, *args, None) == NULL
+    assert f(4, 64, 64, ODD, FAKE, FAKE, FAKE, FAKE, None) == ALIGN
+    assert f(4, 64, 64, FAKE, ODD, FAKE, FAKE, FAKE, None) == ALIGN
+    assert f(4, 64, 64, FAKE, FAKE, ODD, FAKE, FAKE, None) == ALIGN
+    assert f(4, 64, 64, FAKE, FAKE, FAKE, FAKE, ODD, None) == ALIGN
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
