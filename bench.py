@@ -4,6 +4,9 @@ One step = one pass of the whole path over one batch of synthetic input:
   prefill: q8_quantize_act (bf16 2048 x 4096) + q8_gemm (M2048 N12288 K4096)
   decode : q8_quantize_act + q8_gemm at M=1 and at M=4 (N12288 K4096), and
            the same step fused, q8_gemm_act (quantise inside the decode kernel)
+  gated FFN step: q8_gemm_swiglu (gate+up product, silu(g)*u, Q8_0 for the
+           down projection) at M2048 with I = 6144 hidden units (2I = 12288,
+           the prefill weight's size), and at M=1 and M=4
 Weights are packed once (not timed).  Packed weight copies are rotated from
 step to step over more than the 256 MB MALL, so weights come from HBM.
 
@@ -112,8 +115,14 @@ def main():
                         qw.view(torch.uint8).view(N, K // 32, 32)], dim=2).contiguous().view(-1)
     del qw, dw
     packed0 = q8.q8_pack_weights(blocks, N, K)
-    del blocks
     packs = [packed0] + [packed0.clone() for _ in range(args.rotate - 1)]
+    # gate/up weight of I = N/2 hidden units: the same rows, read as gate
+    # (first half) and up (second half)
+    I = N // 2
+    bl = blocks.view(N, -1)
+    gu0 = q8.q8_pack_weights_gateup(bl[:I].contiguous().view(-1), bl[I:].contiguous().view(-1), I, K)
+    gus = [gu0] + [gu0.clone() for _ in range(args.rotate - 1)]
+    del blocks, bl
     xp = torch.from_numpy(workloads.activations(pre).view(np.int16)).to(dev).view(torch.bfloat16)
     x4 = torch.from_numpy(workloads.activations(dec4).view(np.int16)).to(dev).view(torch.bfloat16)
     x1 = x4[:1]
@@ -127,9 +136,15 @@ def main():
     d1 = torch.empty((1, K // 32), dtype=torch.float16, device=dev)
     C4 = torch.empty((4, N), dtype=torch.float32, device=dev)
     C1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+    qh = torch.empty((M, I), dtype=torch.int8, device=dev)
+    dh = torch.empty((M, I // 32), dtype=torch.float16, device=dev)
+    qh4 = torch.empty((4, I), dtype=torch.int8, device=dev)
+    dh4 = torch.empty((4, I // 32), dtype=torch.float16, device=dev)
+    qh1 = torch.empty((1, I), dtype=torch.int8, device=dev)
+    dh1 = torch.empty((1, I // 32), dtype=torch.float16, device=dev)
 
     names = ["quant_prefill", "gemm_prefill", "quant_dec1", "gemv_dec1", "quant_dec4", "gemv_dec4",
-             "fused_dec1", "fused_dec4"]
+             "fused_dec1", "fused_dec4", "swiglu_prefill", "swiglu_dec1", "swiglu_dec4"]
 
     def step(i, ev=None):
         wp = packs[i % len(packs)]
@@ -142,6 +157,9 @@ def main():
             lambda: q8.q8_gemm(q4, d4, packs[(i + 5) % len(packs)], N, K, out=C4),
             lambda: q8.q8_gemm_act(x1, packs[(i + 2) % len(packs)], N, K, out=C1),
             lambda: q8.q8_gemm_act(x4, packs[(i + 6) % len(packs)], N, K, out=C4),
+            lambda: q8.q8_gemm_swiglu(qa, da, gus[i % len(gus)], I, K, q=qh, d=dh),
+            lambda: q8.q8_gemm_swiglu(q1, d1, gus[(i + 3) % len(gus)], I, K, q=qh1, d=dh1),
+            lambda: q8.q8_gemm_swiglu(q4, d4, gus[(i + 5) % len(gus)], I, K, q=qh4, d=dh4),
         ]
         for j, c in enumerate(calls):
             if ev is not None:
@@ -198,6 +216,10 @@ def main():
         "gemv_dec4": block_us(lambda i: q8.q8_gemm(q4, d4, packs[i % P], N, K, out=C4), C4),
         "fused_dec1": block_us(lambda i: q8.q8_gemm_act(x1, packs[i % P], N, K, out=C1), C1),
         "fused_dec4": block_us(lambda i: q8.q8_gemm_act(x4, packs[i % P], N, K, out=C4), C4),
+        "swiglu_dec1": block_us(lambda i: q8.q8_gemm_swiglu(q1, d1, gus[i % P], I, K, q=qh1, d=dh1),
+                                qh1),
+        "swiglu_dec4": block_us(lambda i: q8.q8_gemm_swiglu(q4, d4, gus[i % P], I, K, q=qh4, d=dh4),
+                                qh4),
     }
 
     dur = {n: np.array([events[i][j][0].elapsed_time(events[i][j][1]) for i in range(args.steps)])
@@ -242,6 +264,17 @@ def main():
                 "algorithmic_ops_per_launch": ops,
                 "epilogue_ceiling_frac": 0.25}
 
+    sw_us = mean["swiglu_prefill"] * 1e3
+    swiglu = {"workload": "M2048 I6144 K4096 (gate+up 12288 x 4096)",
+              "kernel_us": round(sw_us, 2),
+              "tops": round(2.0 * M * 2 * I * K / (sw_us * 1e-6) / 1e12, 1),
+              "plain_gemm_same_shape_us": round(mean["gemm_prefill"] * 1e3, 2),
+              "output_bytes": M * I + M * (I // 32) * 2,
+              "plain_gemm_output_bytes": M * 2 * I * 4,
+              "decode_M1_us": round(back["swiglu_dec1"], 2),
+              "decode_M4_us": round(back["swiglu_dec4"], 2),
+              "traffic": measured_traffic("swiglu_prefill_traffic.json", "q8_gemm.hip", None)}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds, qa, da, packs, N, K)
@@ -258,6 +291,7 @@ def main():
                    "quantize_prefill_us": round(mean["quant_prefill"] * 1e3, 2)},
         "roofline": roofline,
         "decode": dec,
+        "swiglu": swiglu,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
