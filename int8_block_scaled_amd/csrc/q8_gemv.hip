@@ -156,7 +156,12 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_slice_kernel(
   const int nwaves = blockDim.x >> 6;
   const int64_t kb0 = static_cast<int64_t>(wave) * kb_per_wave;
   const int64_t kb1 = kb0 + kb_per_wave < KB ? kb0 + kb_per_wave : KB;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * rows;
+  // Slices that share a row group share 128-byte lines of its scale plane:
+  // keep neighbours on one XCD (workgroup i runs on XCD i % 8) so that the
+  // line comes from HBM once, into that XCD's L2.
+  int slice = blockIdx.x;
+  if (gridDim.x % 8 == 0) slice = (slice & 7) * (gridDim.x >> 3) + (slice >> 3);
+  const int64_t n0 = static_cast<int64_t>(slice) * rows;
   // the row this lane loads: its own, or the slice's last; never past N - 1
   // (when N is a multiple of 64 the packed layout has no padding rows)
   int64_t n = n0 + (lane < rows ? lane : rows - 1);
@@ -264,8 +269,10 @@ __global__ __launch_bounds__(kThreads) void gemv_q8_act_kernel(
   const int64_t kb0 = static_cast<int64_t>(wave) * kb_per_wave;
   const int64_t kb1 = kb0 + kb_per_wave < KB ? kb0 + kb_per_wave : KB;
   const bool store_q = q_out != nullptr && blockIdx.x == 0;
-  // rows as in gemv_q8_slice_kernel
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * rows;
+  // rows (and their order over the XCDs) as in gemv_q8_slice_kernel
+  int slice = blockIdx.x;
+  if (gridDim.x % 8 == 0) slice = (slice & 7) * (gridDim.x >> 3) + (slice >> 3);
+  const int64_t n0 = static_cast<int64_t>(slice) * rows;
   int64_t n = n0 + (lane < rows ? lane : rows - 1);
   n = n < N ? n : N - 1;
   const int64_t g = n >> 6, r = n & 63;
