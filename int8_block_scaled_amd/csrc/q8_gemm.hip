@@ -468,14 +468,27 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // XCD-aware order: hardware id i lands on XCD i % 8; give each XCD a
-  // contiguous range of logical tiles (M-fastest within the range).
-  int bid = blockIdx.x;
-  if (remap) {
-    const int per = gridDim.x >> 3;
-    bid = (bid & 7) * per + (bid >> 3);
+  // XCD-aware order: hardware id i lands on XCD i % 8.  remap == 1: each
+  // XCD takes a contiguous range of logical tiles (M-fastest within it).
+  // remap == sm in {2, 4, 8}: the tile grid is cut into sm x (8/sm)
+  // rectangles, one per XCD (M-fastest within it), so that an XCD's
+  // activation rows fit its L2 and are fetched once.
+  int tm, tn;
+  if (remap >= 2) {
+    const int sm = remap, sn = 8 / sm;
+    const int tmx = tiles_m / sm, tnx = static_cast<int>(gridDim.x) / tiles_m / sn;
+    const int x = blockIdx.x & 7, local = blockIdx.x >> 3;
+    tm = (x % sm) * tmx + local % tmx;
+    tn = (x / sm) * tnx + local / tmx;
+  } else {
+    int bid = blockIdx.x;
+    if (remap) {
+      const int per = gridDim.x >> 3;
+      bid = (bid & 7) * per + (bid >> 3);
+    }
+    tm = bid % tiles_m;
+    tn = bid / tiles_m;
   }
-  const int tm = bid % tiles_m, tn = bid / tiles_m;
   const int64_t m0 = static_cast<int64_t>(tm) * BM;
   const int64_t n0 = static_cast<int64_t>(tn) * BN;
   const int64_t g0 = n0 / kGroupRows;
@@ -620,7 +633,18 @@ hipError_t launch_tile_impl(int64_t M, int64_t N, int64_t K, const int8_t* q_a,
   const int64_t tiles_m = (M + T::BM - 1) / T::BM;
   const int64_t tiles_n = (N + T::BN - 1) / T::BN;
   const int64_t grid = tiles_m * tiles_n;
-  const int remap = (grid % 8 == 0) ? 1 : 0;
+  int remap = (grid % 8 == 0) ? 1 : 0;
+  // The activation rows an XCD needs (BM*K bytes per tile row) should stay
+  // in its 4 MB L2: if all tiles_m rows do not fit, split M over sm XCDs.
+  constexpr int64_t kL2Bytes = 4 << 20;
+  if (remap && tiles_m * T::BM * K > kL2Bytes) {
+    for (int sm = 2; sm <= 8; sm *= 2)
+      if (tiles_m % sm == 0 && tiles_n % (8 / sm) == 0 && tiles_m / sm * T::BM * K <= kL2Bytes) {
+        remap = sm;
+        break;
+      }
+  }
+  if (const char* e = getenv("Q8_GEMM_REMAP")) remap = atoi(e);   // benchmarking aid
   hipLaunchKernelGGL((gemm_q8_mfma_kernel<T, kOcc, kSwiglu>), dim3(static_cast<uint32_t>(grid)),
                      dim3(T::kThreads), 0, stream, q_a, d_a, w_packed, ws, C, M, N, K, KB, NG,
                      ldc, static_cast<int>(tiles_m), remap, q_h, d_h);
