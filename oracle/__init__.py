@@ -52,6 +52,14 @@ def _bind(L):
     L.q8ref_silu.restype = ctypes.c_double
     L.q8ref_swiglu_quant.argtypes = [i64, i64, vp, vp, vp, vp, vp]
     L.q8ref_swiglu_quant.restype = None
+    L.q8ref_kv3_levels.argtypes = [vp]
+    L.q8ref_kv3_levels.restype = None
+    L.q8ref_fwht.argtypes = [vp, ctypes.c_int]
+    L.q8ref_fwht.restype = None
+    L.q8ref_kv3_encode.argtypes = [vp, ctypes.c_int, i64, ctypes.c_int, i64, vp, vp]
+    L.q8ref_kv3_encode.restype = None
+    L.q8ref_kv3_decode.argtypes = [vp, vp, i64, ctypes.c_int, vp]
+    L.q8ref_kv3_decode.restype = None
     L.q8ref_num_threads.argtypes = []
     L.q8ref_num_threads.restype = ctypes.c_int
     return L
@@ -209,6 +217,39 @@ class Oracle:
         """GGUF Q8_0 bytes of the gate and up weights ([I][K/32*34] each) ->
         the packed layout of their interleaved rows (2I rows)."""
         return self.pack(self.interleave_gateup(gate_blocks, up_blocks), 2 * I, K)
+
+    # ---- 3-bit KV-cache codec -------------------------------------------
+
+    def kv3_levels(self) -> np.ndarray:
+        out = np.empty(8, dtype=np.float32)
+        self.L.q8ref_kv3_levels(_p(out))
+        return out
+
+    def fwht(self, v) -> np.ndarray:
+        """Unnormalised Walsh-Hadamard transform of one binary32 vector."""
+        v = np.array(v, dtype=np.float32, copy=True)
+        self.L.q8ref_fwht(_p(v), v.size)
+        return v
+
+    def kv3_encode(self, x, D=None):
+        """Rows of x ([R][>=D] float32, or uint16 bfloat16 bits) ->
+        (codes uint8 [R][3D/8], scales float32 [R])."""
+        dtype = 1 if x.dtype == np.uint16 else 0
+        x = _c(x, np.uint16 if dtype else np.float32)
+        R, ldx = x.shape
+        D = ldx if D is None else D
+        assert D in (64, 128, 256) and D <= ldx
+        codes = np.empty((R, 3 * D // 8), dtype=np.uint8)
+        scales = np.empty(R, dtype=np.float32)
+        self.L.q8ref_kv3_encode(_p(x), dtype, R, D, ldx, _p(codes), _p(scales))
+        return codes, scales
+
+    def kv3_decode(self, codes, scales, D) -> np.ndarray:
+        codes, scales = _c(codes, np.uint8), _c(scales, np.float32)
+        R = codes.shape[0]
+        out = np.empty((R, D), dtype=np.float32)
+        self.L.q8ref_kv3_decode(_p(codes), _p(scales), R, D, _p(out))
+        return out
 
     def num_threads(self) -> int:
         return int(self.L.q8ref_num_threads())

@@ -363,6 +363,110 @@ void q8ref_swiglu_quant(int64_t M, int64_t I, const double *G, const double *U,
         }
 }
 
+/* ------------------------------------------------------------------------ */
+/* 3-bit KV-cache codec (the pages' "3-bit KV cache (WHT + Lloyd-Max)",     */
+/* 17 GB -> 3.5 GB at 256K context; the pages give no more detail, so the   */
+/* format below is the plainest reading, written from its description in    */
+/* the library header):                                                     */
+/*   a row x of D values (D = 64, 128 or 256) is transformed by the         */
+/*   unnormalised Sylvester Hadamard matrix, y = H x, with the radix-2      */
+/*   butterfly in binary32 (stages len = 1, 2, 4, ..., D/2; a pair (i,      */
+/*   i+len) becomes (a+b, a-b));                                            */
+/*   s = sqrt(S/D) with S the sum of y_i^2 by the pairwise tree (len = D/2,  */
+/*   D/4, ..., 1: v_i += v_{i+len} for i < len), binary32, correctly        */
+/*   rounded sqrt; u_i = y_i * (1/s);                                       */
+/*   code_i = the number of decision thresholds t_k <= u_i, the thresholds  */
+/*   being the binary32 midpoints (L_k + L_{k+1}) * 0.5 of the codebook L   */
+/*   (the 8-level Lloyd-Max quantiser of a unit Gaussian, levels +-0.2451,  */
+/*   +-0.7560, +-1.3440, +-2.1520 as binary32);                             */
+/*   rows with s < FLT_MIN get every code 4 and s = 0;                      */
+/*   8 codes pack into 3 bytes little-endian, code j of a group at bits     */
+/*   3j..3j+2; decode: z_i = s * L[code_i], x^ = (H z) * (1/D).             */
+/* ------------------------------------------------------------------------ */
+
+static const float kv3_levels[8] = {-2.1520f, -1.3440f, -0.7560f, -0.2451f,
+                                    0.2451f,  0.7560f,  1.3440f,  2.1520f};
+
+void q8ref_kv3_levels(float *out)
+{
+    for (int i = 0; i < 8; ++i) out[i] = kv3_levels[i];
+}
+
+/* In-place binary32 fast Walsh-Hadamard transform (unnormalised). */
+void q8ref_fwht(float *v, int D)
+{
+    for (int len = 1; len < D; len <<= 1)
+        for (int i = 0; i < D; i += 2 * len)
+            for (int j = i; j < i + len; ++j) {
+                float a = v[j], b = v[j + len];
+                v[j] = a + b;
+                v[j + len] = a - b;
+            }
+}
+
+static int kv3_code(float u)
+{
+    int c = 0;
+    for (int k = 0; k < 7; ++k) {
+        float t = (kv3_levels[k] + kv3_levels[k + 1]) * 0.5f;
+        if (t <= u) ++c;
+    }
+    return c;
+}
+
+/* x: [R][ldx] binary32 (dtype 0) or bfloat16 bits (dtype 1).
+ * codes: [R][3D/8] bytes; scales: [R] binary32. */
+void q8ref_kv3_encode(const void *x, int dtype, int64_t R, int D, int64_t ldx,
+                      uint8_t *codes, float *scales)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        float y[256], v[256];
+        for (int i = 0; i < D; ++i)
+            y[i] = dtype == 1 ? q8ref_bf16_to_f32(((const uint16_t *)x)[r * ldx + i])
+                              : ((const float *)x)[r * ldx + i];
+        q8ref_fwht(y, D);
+        for (int i = 0; i < D; ++i) v[i] = y[i] * y[i];
+        for (int len = D / 2; len >= 1; len >>= 1)
+            for (int i = 0; i < len; ++i) v[i] = v[i] + v[i + len];
+        float s = sqrtf(v[0] / (float)D);
+        uint8_t *out = codes + r * (3 * D / 8);
+        memset(out, 0, (size_t)(3 * D / 8));
+        if (!(s >= FLT_MIN)) {
+            s = 0.0f;
+            for (int i = 0; i < D; ++i) y[i] = 0.0f;   /* code 4 below */
+        }
+        float inv = s > 0.0f ? 1.0f / s : 0.0f;
+        for (int g = 0; g < D / 8; ++g) {
+            uint32_t w = 0;
+            for (int j = 0; j < 8; ++j) {
+                int c = kv3_code(y[8 * g + j] * inv);
+                w |= (uint32_t)c << (3 * j);
+            }
+            out[3 * g + 0] = (uint8_t)(w & 0xff);
+            out[3 * g + 1] = (uint8_t)((w >> 8) & 0xff);
+            out[3 * g + 2] = (uint8_t)((w >> 16) & 0xff);
+        }
+        scales[r] = s;
+    }
+}
+
+/* codes, scales as written by q8ref_kv3_encode -> out [R][D] binary32. */
+void q8ref_kv3_decode(const uint8_t *codes, const float *scales, int64_t R, int D, float *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        float z[256];
+        const uint8_t *in = codes + r * (3 * D / 8);
+        for (int g = 0; g < D / 8; ++g) {
+            uint32_t w = in[3 * g] | ((uint32_t)in[3 * g + 1] << 8) | ((uint32_t)in[3 * g + 2] << 16);
+            for (int j = 0; j < 8; ++j) z[8 * g + j] = scales[r] * kv3_levels[(w >> (3 * j)) & 7u];
+        }
+        q8ref_fwht(z, D);
+        for (int i = 0; i < D; ++i) out[r * D + i] = z[i] * (1.0f / (float)D);
+    }
+}
+
 /* Threads the OpenMP runtime will use (for reporting the CPU baseline). */
 int q8ref_num_threads(void)
 {

@@ -22,6 +22,8 @@ import os
 import struct
 from fractions import Fraction
 
+import math
+
 import numpy as np
 
 from oracle import exact
@@ -435,7 +437,126 @@ def pin_gateup_layout(orc):
         assert sp[(g * KB + kb) * 64 + rr] == srcd[32 * g + rr % 32, kb]
 
 
+# --------------------------------------------------------------------------
+# 3-bit KV-cache codec
+# --------------------------------------------------------------------------
+
+def _phi(x):
+    return math.exp(-0.5 * x * x) / math.sqrt(2 * math.pi) if math.isfinite(x) else 0.0
+
+
+def _Phi(x):
+    return 0.5 * (1.0 + math.erf(x / math.sqrt(2.0))) if math.isfinite(x) else (1.0 if x > 0 else 0.0)
+
+
+def pin_kv3_codebook(orc):
+    """The codebook is the 8-level Lloyd-Max quantiser of a unit Gaussian:
+    symmetric, and each level is the centroid E[X | cell] of its cell, the
+    cells being cut at the midpoints of adjacent levels (closed form:
+    (phi(a) - phi(b)) / (Phi(b) - Phi(a))); the levels are given to 4
+    decimals, so to 5e-4."""
+    L = orc.kv3_levels().astype(np.float64)
+    assert np.all(np.diff(L) > 0) and np.allclose(L, -L[::-1], atol=0, rtol=0)
+    t = [-math.inf] + [(L[k] + L[k + 1]) / 2 for k in range(7)] + [math.inf]
+    for k in range(8):
+        a, b = t[k], t[k + 1]
+        c = (_phi(a) - _phi(b)) / (_Phi(b) - _Phi(a))
+        assert abs(c - L[k]) < 5e-4, (k, L[k], c)
+
+
+def _sylvester(D):
+    H = np.array([[1.0]])
+    while H.shape[0] < D:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def pin_fwht(orc):
+    """The binary32 butterfly equals the Sylvester Hadamard matrix: exactly
+    on unit vectors and small integers (then H H x = D x exactly too), and
+    within its rounding bound on random vectors."""
+    for D in (64, 128, 256):
+        H = _sylvester(D)
+        for k in (0, 1, 5, D - 1):
+            e = np.zeros(D, np.float32)
+            e[k] = 1
+            assert np.array_equal(orc.fwht(e), H[:, k].astype(np.float32))
+        r = np.random.default_rng(D)
+        xi = r.integers(-50, 51, D).astype(np.float32)
+        assert np.array_equal(orc.fwht(xi), (H @ xi).astype(np.float32))
+        assert np.array_equal(orc.fwht(orc.fwht(xi)), (D * xi).astype(np.float32))
+        x = r.standard_normal(D).astype(np.float32)
+        ref = H @ x.astype(np.float64)
+        assert np.all(np.abs(orc.fwht(x) - ref) <= D * 2.0 ** -24 * np.abs(x).sum() + 1e-30)
+
+
+def pin_kv3_golden(orc):
+    """Hand-derived rows (D = 128).  e_0: y = all ones, s = 1, every u = 1,
+    code 5 (level 0.7560), bytes 6D DB B6 repeated, decode 0.756 e_0.  A
+    column h_k of H: y = 128 e_k, s = sqrt(128), code 7 at k and code 4
+    (u = 0 sits on the middle threshold) elsewhere.  The zero row: every
+    code 4 (bytes 24 49 92), s = 0, decode 0."""
+    D = 128
+    H = _sylvester(D).astype(np.float32)
+    x = np.zeros((3, D), np.float32)
+    x[0, 0] = 1.0
+    x[1] = H[:, 37]
+    codes, scales = orc.kv3_encode(x)
+    assert list(codes[0]) == [0x6D, 0xDB, 0xB6] * 16 and scales[0] == 1.0
+    assert scales[1] == np.float32(math.sqrt(128.0))
+    want = [4] * D
+    want[37] = 7
+    w = [sum(want[8 * g + j] << (3 * j) for j in range(8)) for g in range(16)]
+    assert list(codes[1]) == [b for v in w for b in (v & 255, (v >> 8) & 255, v >> 16)]
+    assert list(codes[2]) == [0x24, 0x49, 0x92] * 16 and scales[2] == 0.0
+    out = orc.kv3_decode(codes, scales, D)
+    e0 = np.zeros(D, np.float32)
+    e0[0] = np.float32(0.7560)
+    assert np.array_equal(out[0], e0) and not np.any(out[2])
+
+
+def pin_kv3_code_positions(orc):
+    """Code j of a 3-byte group sits at bits 3j..3j+2: decoding rows with a
+    single non-middle code at a known position gives back, through the
+    transform (H x^ = z), the level at exactly that position."""
+    D = 64
+    L = orc.kv3_levels()
+    for pos, c in [(0, 0), (7, 7), (8, 1), (21, 6), (63, 2)]:
+        codes4 = [4] * D
+        codes4[pos] = c
+        w = [sum(codes4[8 * g + j] << (3 * j) for j in range(8)) for g in range(D // 8)]
+        row = np.array([b for v in w for b in (v & 255, (v >> 8) & 255, v >> 16)], np.uint8)
+        out = orc.kv3_decode(row[None, :], np.array([2.0], np.float32), D)[0]
+        z = orc.fwht(out)
+        want = np.full(D, 2.0 * L[4], np.float64)
+        want[pos] = 2.0 * L[c]
+        assert np.all(np.abs(z - want) < 1e-5), (pos, c)
+
+
+def pin_kv3_roundtrip(orc):
+    """Gaussian rows: the relative mean squared error of decode(encode(x))
+    is that of the 3-bit Lloyd-Max quantiser of a Gaussian (about 0.0345);
+    scaling a row by a power of two scales s and nothing else; a bf16 row
+    codes as its exact binary32 widening."""
+    r = np.random.default_rng(40)
+    for D in (64, 128, 256):
+        x = r.standard_normal((1500, D)).astype(np.float32)
+        codes, scales = orc.kv3_encode(x)
+        xh = orc.kv3_decode(codes, scales, D)
+        nmse = float(np.mean((xh - x) ** 2) / np.mean(x ** 2))
+        assert 0.030 < nmse < 0.038, (D, nmse)
+        c2, s2 = orc.kv3_encode(x * np.float32(8.0))
+        assert np.array_equal(c2, codes) and np.array_equal(s2, scales * np.float32(8.0))
+    xb = np.frombuffer(r.standard_normal((40, 128)).astype(np.float32).tobytes(), np.uint32)
+    bits = (xb >> 16).astype(np.uint16).reshape(40, 128)
+    wide = (bits.astype(np.uint32) << 16).view(np.float32)
+    ca, sa = orc.kv3_encode(bits)
+    cb, sb = orc.kv3_encode(wide)
+    assert np.array_equal(ca, cb) and np.array_equal(sa, sb)
+
+
 ALL_PINS = [pin_f16_roundtrip_all, pin_f16_vs_numpy, pin_quant_golden, pin_quant_exact_random,
             pin_quant_invariants, pin_quant_rows, pin_gemm_golden, pin_gemm_exact,
             pin_gemm_unit_scale, pin_block_dots, pin_gemm_sampled, pin_block_bytes,
-            pin_pack_layout, pin_silu, pin_swiglu_golden, pin_swiglu_rows, pin_gateup_layout]
+            pin_pack_layout, pin_silu, pin_swiglu_golden, pin_swiglu_rows, pin_gateup_layout,
+            pin_kv3_codebook, pin_fwht, pin_kv3_golden, pin_kv3_code_positions, pin_kv3_roundtrip]

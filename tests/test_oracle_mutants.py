@@ -41,6 +41,13 @@ MUTANTS = {
                                "double v = q8ref_silu(U[i]) * G[i];"),
     "silu_sign": ("return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
     "swiglu_scale_index": ("d + m * (I / QK) + b);", "d + b * M + m);"),
+    "kv3_threshold_is_level": ("float t = (kv3_levels[k] + kv3_levels[k + 1]) * 0.5f;",
+                               "float t = kv3_levels[k + 1];"),
+    "kv3_butterfly_sign": ("v[j + len] = a - b;", "v[j + len] = b - a;"),
+    "kv3_scale_no_sqrt": ("float s = sqrtf(v[0] / (float)D);", "float s = v[0] / (float)D;"),
+    "kv3_pack_stride": ("w |= (uint32_t)c << (3 * j);", "w |= (uint32_t)c << (3 * (7 - j));"),
+    "kv3_decode_norm": ("out[r * D + i] = z[i] * (1.0f / (float)D);", "out[r * D + i] = z[i];"),
+    "kv3_level_value": ("0.2451f,  0.7560f,", "0.2451f,  0.7650f,"),
 }
 
 
