@@ -4,6 +4,9 @@ One step = one pass of the whole path over one batch of synthetic input:
   prefill: q8_quantize_act (bf16 2048 x 4096) + q8_gemm (M2048 N12288 K4096)
   decode : q8_quantize_act + q8_gemm at M=1 and at M=4 (N12288 K4096), and
            the same step fused, q8_gemm_act (quantise inside the decode kernel)
+  (after the timed steps, apart from them: the 3-bit KV-cache codec,
+           q8_kv3_encode / q8_kv3_decode, on one layer's K and V at 256K
+           context, in "kv3")
   gated FFN step: q8_gemm_swiglu (gate+up product, silu(g)*u, Q8_0 for the
            down projection) at M2048 with I = 6144 hidden units (2I = 12288,
            the prefill weight's size), and at M=1 and M=4
@@ -275,6 +278,8 @@ def main():
               "decode_M4_us": round(back["swiglu_dec4"], 2),
               "traffic": measured_traffic("swiglu_prefill_traffic.json", "q8_gemm.hip", None)}
 
+    kv3 = kv3_bench(q8, workloads, torch, np, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds, qa, da, packs, N, K)
@@ -292,9 +297,55 @@ def main():
         "roofline": roofline,
         "decode": dec,
         "swiglu": swiglu,
+        "kv3": kv3,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def kv3_bench(q8, workloads, torch, np, dev, reps=20):
+    """The 3-bit KV-cache codec on one layer's keys and values at 256K
+    context: 262144 tokens x 4 KV heads x (K, V) = 2^21 rows of D = 256,
+    bfloat16 (1.07 GB, far above the 256 MB MALL, so every launch streams
+    from HBM).  Each launch is timed with an event pair on the stream it runs
+    on; algorithmic bytes are the rows read plus the codes and scales written
+    (encode), and the reverse (decode)."""
+    R, D = 262144 * 8, 256
+    x = workloads.kv_rows_device(R, D, 600, dev)
+    codes = torch.empty((R, 3 * D // 8), dtype=torch.uint8, device=dev)
+    scales = torch.empty((R,), dtype=torch.float32, device=dev)
+    out = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(call):
+        for _ in range(3):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3   # us
+
+    enc_us = timed(lambda: q8.q8_kv3_encode(x, codes=codes, scales=scales))
+    dec_us = timed(lambda: q8.q8_kv3_decode(codes, scales, D, out=out))
+    row_bytes_in, row_bytes_packed = 2 * D, 3 * D // 8 + 4
+    alg = R * (row_bytes_in + row_bytes_packed)
+    xf = x[:65536].float()
+    err = (out[:65536].float() - xf).pow(2).sum() / xf.pow(2).sum()
+    return {"workload": "one layer's K and V at 256K context: R %d rows x D %d, bf16 in/out" % (R, D),
+            "encode_us": round(enc_us, 2), "encode_gbs": round(alg / (enc_us * 1e-6) / 1e9, 1),
+            "encode_frac_hbm": round(alg / (enc_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "decode_us": round(dec_us, 2), "decode_gbs": round(alg / (dec_us * 1e-6) / 1e9, 1),
+            "decode_frac_hbm": round(alg / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes_per_launch": alg,
+            "bits_per_element": 8.0 * row_bytes_packed / D,
+            "compression_vs_bf16": round(row_bytes_in / row_bytes_packed, 3),
+            "relative_mse_first_65536_rows": round(float(err), 5),
+            "encode_traffic": measured_traffic("kv3_encode_traffic.json", "q8_kv3.hip", alg),
+            "decode_traffic": measured_traffic("kv3_decode_traffic.json", "q8_kv3.hip", alg)}
 
 
 def cpu_baseline(seconds, qa_t, da_t, packs, N, K):

@@ -211,6 +211,71 @@ q8_status q8_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t *q_a,
                          const uint16_t *d_a, const void *w_packed, int8_t *q_h,
                          uint16_t *d_h, void *stream);
 
+/*
+ * q8_kv3_encode -- compress key or value vectors to 3 bits per element.
+ *
+ * Source: the source engine holds a 256K-token context by storing its KV
+ * cache in 3 bits, transformed by a Walsh-Hadamard transform (WHT) and
+ * quantised with a Lloyd-Max quantiser, which shrinks the cache from 17 GB
+ * to 3.5 GB (news.hada.io topic 29953, list of paths that avoid the
+ * throttled units, KV-cache item).  The pages give no more than that; the
+ * format below is this library's reading of it, defined exactly so that
+ * every implementation of it produces the same bits.
+ *
+ * Operation, per row x of D values (bfloat16 is widened exactly):
+ *   y = H x, the unnormalised WHT, computed in binary32 as the radix-2
+ *       butterfly: for len = 1, 2, 4, ..., D/2, for every i with
+ *       (i & len) == 0: (y_i, y_{i+len}) <- (y_i + y_{i+len}, y_i - y_{i+len});
+ *   S = sum of y_i^2: the squares, then for len = D/2, D/4, ..., 1:
+ *       v_i <- v_i + v_{i+len} for i < len; S = v_0 (all binary32);
+ *   s = sqrtf(S / D)  (correctly rounded; the RMS of y, so y/s has unit
+ *       variance, the Gaussian the quantiser is designed for);
+ *   if s < FLT_MIN (a zero row, binary32 underflow, or NaN): s = 0 and
+ *       every code is 4;
+ *   else u_i = y_i * (1/s) (the reciprocal correctly rounded) and code_i =
+ *       the number of thresholds t_k <= u_i, where t_k = (L_k + L_{k+1})/2
+ *       in binary32 and L = {-2.1520, -1.3440, -0.7560, -0.2451, 0.2451,
+ *       0.7560, 1.3440, 2.1520} (binary32 nearest) are the levels of the
+ *       8-level Lloyd-Max quantiser of a unit Gaussian.
+ * No operation is fused (no fma).
+ *
+ * Storage: codes [R][3D/8] bytes; code i of a row sits at bits 3*(i % 8)
+ * of the little-endian 24-bit word in bytes 3*(i/8) .. 3*(i/8)+2 of the
+ * row.  scales [R] binary32 (s).  3.125 bits per element at D = 128.
+ *
+ * x      [R][ldx] binary32 or bfloat16 (dtype); 16-byte aligned,
+ *        ldx >= D, ldx*elem % 16 == 0.
+ * R      rows (tokens x heads), R >= 0; R == 0 is a no-op.
+ * D      head dimension: 64, 128 or 256.
+ * codes  out, [R][3D/8] bytes, any alignment.
+ * scales out, [R] binary32, 4-byte aligned.
+ *
+ * Errors: Q8_ERR_NULL, Q8_ERR_SHAPE (D not 64/128/256, R < 0, ldx < D, R
+ * too large to launch), Q8_ERR_ALIGN, Q8_ERR_DTYPE, Q8_ERR_DEVICE,
+ * Q8_ERR_LAUNCH.
+ */
+q8_status q8_kv3_encode(const void *x, q8_dtype dtype, int64_t R, int64_t D, int64_t ldx,
+                        uint8_t *codes, float *scales, void *stream);
+
+/*
+ * q8_kv3_decode -- expand 3-bit KV rows written by q8_kv3_encode.
+ *
+ * Operation, per row: z_i = s * L[code_i] (binary32), then the same
+ * butterfly as the encoder (H is its own inverse up to a factor D), then
+ * out_i = z_i * (1/D).  For out_dtype Q8_BF16 the binary32 result is
+ * rounded to bfloat16, nearest-even.
+ *
+ * codes, scales  as written by q8_kv3_encode for the same D.
+ * R, D   as for q8_kv3_encode.
+ * out    [R][ldo] of out_dtype; 16-byte aligned, ldo >= D,
+ *        ldo*elem % 16 == 0.
+ *
+ * Errors: Q8_ERR_NULL, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DTYPE,
+ * Q8_ERR_DEVICE, Q8_ERR_LAUNCH.
+ */
+q8_status q8_kv3_decode(const uint8_t *codes, const float *scales, int64_t R, int64_t D,
+                        q8_dtype out_dtype, void *out, int64_t ldo, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *q8_status_string(q8_status s);
 

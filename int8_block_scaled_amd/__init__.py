@@ -27,7 +27,8 @@ Q8_F32, Q8_BF16 = 0, 1
 STATUS = {0: "Q8_OK", 1: "Q8_ERR_NULL", 2: "Q8_ERR_SHAPE", 3: "Q8_ERR_ALIGN",
           4: "Q8_ERR_DTYPE", 5: "Q8_ERR_SIZE", 6: "Q8_ERR_DEVICE", 7: "Q8_ERR_LAUNCH"}
 EXPORTS = ("q8_pack_weights", "q8_quantize_act", "q8_gemm", "q8_gemm_act",
-           "q8_pack_weights_gateup", "q8_gemm_swiglu", "q8_status_string")
+           "q8_pack_weights_gateup", "q8_gemm_swiglu", "q8_kv3_encode", "q8_kv3_decode",
+           "q8_status_string")
 
 _lib = None
 
@@ -61,6 +62,10 @@ def _load():
         L.q8_pack_weights_gateup.restype = ctypes.c_int
         L.q8_gemm_swiglu.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.q8_gemm_swiglu.restype = ctypes.c_int
+        L.q8_kv3_encode.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp]
+        L.q8_kv3_encode.restype = ctypes.c_int
+        L.q8_kv3_decode.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp, i64, vp]
+        L.q8_kv3_decode.restype = ctypes.c_int
         L.q8_status_string.argtypes = [ctypes.c_int]
         L.q8_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -254,3 +259,48 @@ def q8_gemm_swiglu(q_a: torch.Tensor, d_a: torch.Tensor, w_packed: torch.Tensor,
     _check("q8_gemm_swiglu", _load().q8_gemm_swiglu(M, I, K, _ptr(q_a), _ptr(d_a), _ptr(w_packed),
                                                     _ptr(q), _ptr(d), _stream(q_a)))
     return q, d
+
+
+def q8_kv3_encode(x: torch.Tensor, codes: torch.Tensor = None, scales: torch.Tensor = None):
+    """Rows of x (float32 or bfloat16, [R][ldx] with D = x.shape[1] in
+    {64, 128, 256}, unit column stride) -> (codes uint8 [R][3D/8],
+    scales float32 [R]): the 3-bit WHT + Lloyd-Max KV-cache format."""
+    _need_cuda("x", x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    dt = _act_dtype(x)
+    R, D = x.shape
+    ldx = x.stride(0) if R > 1 else max(x.stride(0), D)
+    if codes is None:
+        codes = torch.empty((R, 3 * D // 8), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((R,), dtype=torch.float32, device=x.device)
+    if codes.dtype != torch.uint8 or not codes.is_contiguous() or tuple(codes.shape) != (R, 3 * D // 8):
+        raise TypeError("codes must be contiguous uint8 [R][3D/8]")
+    if scales.dtype != torch.float32 or not scales.is_contiguous() or tuple(scales.shape) != (R,):
+        raise TypeError("scales must be contiguous float32 [R]")
+    _check("q8_kv3_encode", _load().q8_kv3_encode(
+        _ptr(x), dt, R, D, ldx, _ptr(codes), _ptr(scales), _stream(x)))
+    return codes, scales
+
+
+def q8_kv3_decode(codes: torch.Tensor, scales: torch.Tensor, D: int,
+                  dtype: torch.dtype = torch.float32, out: torch.Tensor = None) -> torch.Tensor:
+    """(codes [R][3D/8], scales [R]) from q8_kv3_encode -> rows [R][D] of
+    dtype (float32 or bfloat16)."""
+    for name, t in (("codes", codes), ("scales", scales)):
+        _need_cuda(name, t)
+    R = scales.shape[0] if scales.dim() == 1 else -1
+    if codes.dtype != torch.uint8 or not codes.is_contiguous() or tuple(codes.shape) != (R, 3 * D // 8):
+        raise TypeError("codes must be contiguous uint8 [R][3D/8]")
+    if scales.dtype != torch.float32 or not scales.is_contiguous():
+        raise TypeError("scales must be contiguous float32 [R]")
+    if out is None:
+        out = torch.empty((R, D), dtype=dtype, device=codes.device)
+    odt = _act_dtype(out)
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != R or out.shape[1] < D:
+        raise TypeError("out must be [R][>=D] with unit column stride")
+    ldo = out.stride(0) if R > 1 else max(out.stride(0), D)
+    _check("q8_kv3_decode", _load().q8_kv3_decode(
+        _ptr(codes), _ptr(scales), R, D, odt, _ptr(out), ldo, _stream(codes)))
+    return out

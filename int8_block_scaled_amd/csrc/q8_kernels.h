@@ -45,6 +45,12 @@ hipError_t launch_gemv_act(int M, const void* x, int dtype, int64_t ldx, int64_t
                            const uint8_t* w_packed, float* C, int64_t ldc, int8_t* q_out,
                            uint16_t* d_out, hipStream_t stream);
 
+// 3-bit KV-cache codec (q8_kv3.hip); D in {64, 128, 256}.
+hipError_t launch_kv3_encode(const void* x, int dtype, int64_t R, int64_t D, int64_t ldx,
+                             uint8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_kv3_decode(const uint8_t* codes, const float* scales, int64_t R, int64_t D,
+                             int dtype, void* out, int64_t ldo, hipStream_t stream);
+
 constexpr int kGemvMaxM = 8;       // M <= kGemvMaxM takes the decode kernel
 
 inline int64_t num_groups(int64_t N) { return (N + kGroupRows - 1) / kGroupRows; }

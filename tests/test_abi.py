@@ -18,7 +18,7 @@ OK, NULL, SHAPE, ALIGN, DTYPE, SIZE = 0, 1, 2, 3, 4, 5
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q8_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(q8_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -149,7 +149,50 @@ def test_gemm_swiglu_validation(L):
     assert f(4, 64, 64, FAKE, FAKE, FAKE, FAKE, ODD, None) == ALIGN
 
 
+def test_kv3_encode_validation(L):
+    f = L.q8_kv3_encode
+    #        x   dtype R   D    ldx  codes scales
+    assert f(FAKE, 2, 8, 128, 128, FAKE, FAKE, None) == DTYPE
+    for D in (0, 32, 96, 192, 512):
+        assert f(FAKE, 0, 8, D, 512, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 0, -1, 128, 128, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 0, 8, 128, 120, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 0, 1 << 34, 128, 128, FAKE, FAKE, None) == SHAPE
+    assert f(None, 0, 0, 128, 128, None, None, None) == OK        # R == 0: no-op
+    for i in (0, 5, 6):
+        args = [FAKE, 0, 8, 128, 128, FAKE, FAKE]
+        args[i] = None
+        assert f(*args, None) == NULL
+    assert f(ODD, 0, 8, 128, 128, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, 0, 8, 128, 130, FAKE, FAKE, None) == ALIGN      # 520-byte pitch
+    assert f(FAKE, 1, 8, 128, 132, FAKE, FAKE, None) == ALIGN      # 264-byte pitch
+    assert f(FAKE, 0, 8, 128, 128, FAKE, ODD, None) == ALIGN
+    # codes: any alignment, so an odd codes pointer is not an alignment error
+    # (the call then reaches the device check, which fails without a GPU)
+    assert f(FAKE, 0, 8, 128, 128, ODD, FAKE, None) not in (NULL, SHAPE, ALIGN, DTYPE)
+
+
+def test_kv3_decode_validation(L):
+    f = L.q8_kv3_decode
+    #        codes scales R  D  dtype out  ldo
+    assert f(FAKE, FAKE, 8, 128, 7, FAKE, 128, None) == DTYPE
+    for D in (0, 16, 100, 512):
+        assert f(FAKE, FAKE, 8, D, 0, FAKE, 512, None) == SHAPE
+    assert f(FAKE, FAKE, -2, 128, 0, FAKE, 128, None) == SHAPE
+    assert f(FAKE, FAKE, 8, 256, 0, FAKE, 128, None) == SHAPE
+    assert f(None, None, 0, 64, 0, None, 64, None) == OK
+    for i in (0, 1, 5):
+        args = [FAKE, FAKE, 8, 128, 0, FAKE, 128]
+        args[i] = None
+        assert f(*args, None) == NULL
+    assert f(FAKE, FAKE, 8, 128, 0, ODD, 128, None) == ALIGN
+    assert f(FAKE, FAKE, 8, 128, 1, FAKE, 132, None) == ALIGN
+    assert f(FAKE, ODD, 8, 128, 0, FAKE, 128, None) == ALIGN
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
         q8.q8_quantize_act(torch.zeros(4, 64))
+    with pytest.raises(TypeError):
+        q8.q8_kv3_encode(torch.zeros(4, 128))

@@ -20,7 +20,20 @@ prompts, so every tensor here is drawn from a fixed distribution:
 * "outlier" activations: round(0.01*K) channels (drawn once per layer,
   shared by every row) multiplied by 50 before rounding to bfloat16.
 
-Streams: numpy ``default_rng(SeedSequence([seed, case, tensor]))``.
+KV-cache rows (the 3-bit KV-cache codec, same pages, KV-cache item of the
+engine's list): the pages give only the context length (256K tokens) and the
+bfloat16 size (17 GB).  Rows of D = 256 with 64 rows per token (layers x KV
+heads, keys and values each) reproduce that size: 262144 * 64 * 2 * 256 * 2
+bytes = 17.2 GB.  Each row is
+
+* kv rows      x[r][i] = z * c_i * g_r with z ~ N(0, 1), per-channel gains
+  c_i = exp(0.5 N(0, 1)) (2 % of channels, drawn once per case, times 10:
+  the outlier channels of attention keys) and per-row gains g_r = 2^U(-2, 2),
+  rounded to bfloat16 where the workload is bfloat16.
+
+Streams: numpy ``default_rng(SeedSequence([seed, case, tensor]))``; the
+device generator for full-size KV caches uses torch's Philox stream seeded
+with the same three numbers folded into one.
 """
 from dataclasses import dataclass
 from typing import Optional
@@ -77,6 +90,38 @@ def outlier_channels(K: int, case: int, seed: int = 0, frac: float = 0.01) -> np
     """The round(frac*K) outlier channels of a layer, from their own stream so
     that every M of the same layer shares them."""
     return rng(case, 99, seed).choice(K, size=int(round(frac * K)), replace=False)
+
+
+def kv_channel_gains(D: int, case: int, seed: int = 0) -> np.ndarray:
+    r = rng(case, 98, seed)
+    c = np.exp(0.5 * r.standard_normal(D)).astype(np.float32)
+    c[r.choice(D, size=max(1, int(round(0.02 * D))), replace=False)] *= np.float32(10.0)
+    return c
+
+
+def kv_rows(R: int, D: int, case: int, tensor: int = 3, seed: int = 0) -> np.ndarray:
+    """[R][D] float32 KV-cache rows (see the module docstring)."""
+    r = rng(case, tensor, seed)
+    z = r.standard_normal((R, D), dtype=np.float32)
+    g = np.exp2(r.uniform(-2.0, 2.0, (R, 1))).astype(np.float32)
+    return z * kv_channel_gains(D, case, seed)[None, :] * g
+
+
+def kv_rows_device(R: int, D: int, case: int, device, tensor: int = 3, seed: int = 0):
+    """The same distribution as kv_rows, drawn on the device as bfloat16 (for
+    caches too large to draw on the host); a different stream from kv_rows."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed((seed * 1000003 + case) * 1000003 + tensor)
+    c = torch.from_numpy(kv_channel_gains(D, case, seed)).to(device)
+    out = torch.empty((R, D), dtype=torch.bfloat16, device=device)
+    step = 1 << 20
+    for r0 in range(0, R, step):
+        r1 = min(R, r0 + step)
+        z = torch.randn((r1 - r0, D), generator=gen, device=device, dtype=torch.float32)
+        g = torch.exp2(torch.rand((r1 - r0, 1), generator=gen, device=device) * 4.0 - 2.0)
+        out[r0:r1] = (z * c * g).to(torch.bfloat16)
+    return out
 
 
 @dataclass(frozen=True)
