@@ -226,8 +226,10 @@ q8_status q8_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t *q_a,
  *   y = H x, the unnormalised WHT, computed in binary32 as the radix-2
  *       butterfly: for len = 1, 2, 4, ..., D/2, for every i with
  *       (i & len) == 0: (y_i, y_{i+len}) <- (y_i + y_{i+len}, y_i - y_{i+len});
- *   S = sum of y_i^2: the squares, then for len = D/2, D/4, ..., 1:
- *       v_i <- v_i + v_{i+len} for i < len; S = v_0 (all binary32);
+ *   S = sum of y_i^2 by pairwise summation over adjacent pairs: the
+ *       squares v_i = y_i^2, then for len = 1, 2, 4, ..., D/2:
+ *       v_i <- v_i + v_{i+len} for every i that is a multiple of 2 len;
+ *       S = v_0 (all binary32);
  *   s = sqrtf(S / D)  (correctly rounded; the RMS of y, so y/s has unit
  *       variance, the Gaussian the quantiser is designed for);
  *   if s < FLT_MIN (a zero row, binary32 underflow, or NaN): s = 0 and
@@ -247,7 +249,7 @@ q8_status q8_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t *q_a,
  *        ldx >= D, ldx*elem % 16 == 0.
  * R      rows (tokens x heads), R >= 0; R == 0 is a no-op.
  * D      head dimension: 64, 128 or 256.
- * codes  out, [R][3D/8] bytes, any alignment.
+ * codes  out, [R][3D/8] bytes, 16-byte aligned.
  * scales out, [R] binary32, 4-byte aligned.
  *
  * Errors: Q8_ERR_NULL, Q8_ERR_SHAPE (D not 64/128/256, R < 0, ldx < D, R
@@ -265,7 +267,8 @@ q8_status q8_kv3_encode(const void *x, q8_dtype dtype, int64_t R, int64_t D, int
  * out_i = z_i * (1/D).  For out_dtype Q8_BF16 the binary32 result is
  * rounded to bfloat16, nearest-even.
  *
- * codes, scales  as written by q8_kv3_encode for the same D.
+ * codes, scales  as written by q8_kv3_encode for the same D (codes
+ *        16-byte aligned, scales 4-byte aligned).
  * R, D   as for q8_kv3_encode.
  * out    [R][ldo] of out_dtype; 16-byte aligned, ldo >= D,
  *        ldo*elem % 16 == 0.

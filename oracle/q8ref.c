@@ -372,9 +372,10 @@ void q8ref_swiglu_quant(int64_t M, int64_t I, const double *G, const double *U,
 /*   unnormalised Sylvester Hadamard matrix, y = H x, with the radix-2      */
 /*   butterfly in binary32 (stages len = 1, 2, 4, ..., D/2; a pair (i,      */
 /*   i+len) becomes (a+b, a-b));                                            */
-/*   s = sqrt(S/D) with S the sum of y_i^2 by the pairwise tree (len = D/2,  */
-/*   D/4, ..., 1: v_i += v_{i+len} for i < len), binary32, correctly        */
-/*   rounded sqrt; u_i = y_i * (1/s);                                       */
+/*   s = sqrt(S/D) with S the sum of y_i^2 by the pairwise tree over       */
+/*   adjacent pairs (len = 1, 2, 4, ..., D/2: v_i += v_{i+len} for i a      */
+/*   multiple of 2 len), binary32, correctly rounded sqrt;                  */
+/*   u_i = y_i * (1/s);                                                     */
 /*   code_i = the number of decision thresholds t_k <= u_i, the thresholds  */
 /*   being the binary32 midpoints (L_k + L_{k+1}) * 0.5 of the codebook L   */
 /*   (the 8-level Lloyd-Max quantiser of a unit Gaussian, levels +-0.2451,  */
@@ -427,8 +428,8 @@ void q8ref_kv3_encode(const void *x, int dtype, int64_t R, int D, int64_t ldx,
                               : ((const float *)x)[r * ldx + i];
         q8ref_fwht(y, D);
         for (int i = 0; i < D; ++i) v[i] = y[i] * y[i];
-        for (int len = D / 2; len >= 1; len >>= 1)
-            for (int i = 0; i < len; ++i) v[i] = v[i] + v[i + len];
+        for (int len = 1; len < D; len <<= 1)
+            for (int i = 0; i < D; i += 2 * len) v[i] = v[i] + v[i + len];
         float s = sqrtf(v[0] / (float)D);
         uint8_t *out = codes + r * (3 * D / 8);
         memset(out, 0, (size_t)(3 * D / 8));
