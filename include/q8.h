@@ -246,7 +246,7 @@ q8_status q8_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t *q_a,
  * row.  scales [R] binary32 (s).  3.125 bits per element at D = 128.
  *
  * x      [R][ldx] binary32 or bfloat16 (dtype); 16-byte aligned,
- *        ldx >= D, ldx*elem % 16 == 0.
+ *        ldx >= D, ldx*elem % 16 == 0, ldx*elem < 2^25 (32 MiB).
  * R      rows (tokens x heads), R >= 0; R == 0 is a no-op.
  * D      head dimension: 64, 128 or 256.
  * codes  out, [R][3D/8] bytes, 16-byte aligned.
@@ -271,7 +271,7 @@ q8_status q8_kv3_encode(const void *x, q8_dtype dtype, int64_t R, int64_t D, int
  *        16-byte aligned, scales 4-byte aligned).
  * R, D   as for q8_kv3_encode.
  * out    [R][ldo] of out_dtype; 16-byte aligned, ldo >= D,
- *        ldo*elem % 16 == 0.
+ *        ldo*elem % 16 == 0, ldo*elem < 2^25 (32 MiB).
  *
  * Errors: Q8_ERR_NULL, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DTYPE,
  * Q8_ERR_DEVICE, Q8_ERR_LAUNCH.

@@ -198,11 +198,14 @@ q8_status q8_gemm_act(const void* x, q8_dtype dtype, int64_t M, int64_t N, int64
 q8_status q8_kv3_encode(const void* x, q8_dtype dtype, int64_t R, int64_t D, int64_t ldx,
                         uint8_t* codes, float* scales, void* stream) {
   if (dtype != Q8_F32 && dtype != Q8_BF16) return Q8_ERR_DTYPE;
-  if (R < 0 || !valid_head_dim(D) || ldx < D || (R + 3) / 4 >= kMaxDim) return Q8_ERR_SHAPE;
+  const int64_t esize = dtype == Q8_F32 ? 4 : 2;
+  if (R < 0 || !valid_head_dim(D) || ldx < D || (R + 3) / 4 >= kMaxDim ||
+      ldx * esize * 64 >= (int64_t(1) << 31))
+    return Q8_ERR_SHAPE;
   if (R == 0) return Q8_OK;
   if (x == nullptr || codes == nullptr || scales == nullptr) return Q8_ERR_NULL;
-  const int64_t esize = dtype == Q8_F32 ? 4 : 2;
-  if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(scales, 4)) return Q8_ERR_ALIGN;
+  if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(codes, 16) || !aligned(scales, 4))
+    return Q8_ERR_ALIGN;
   const q8_status dev = check_device();
   if (dev != Q8_OK) return dev;
   return q8::launch_kv3_encode(x, static_cast<int>(dtype), R, D, ldx, codes, scales,
@@ -214,11 +217,14 @@ q8_status q8_kv3_encode(const void* x, q8_dtype dtype, int64_t R, int64_t D, int
 q8_status q8_kv3_decode(const uint8_t* codes, const float* scales, int64_t R, int64_t D,
                         q8_dtype out_dtype, void* out, int64_t ldo, void* stream) {
   if (out_dtype != Q8_F32 && out_dtype != Q8_BF16) return Q8_ERR_DTYPE;
-  if (R < 0 || !valid_head_dim(D) || ldo < D || (R + 3) / 4 >= kMaxDim) return Q8_ERR_SHAPE;
+  const int64_t esize = out_dtype == Q8_F32 ? 4 : 2;
+  if (R < 0 || !valid_head_dim(D) || ldo < D || (R + 3) / 4 >= kMaxDim ||
+      ldo * esize * 64 >= (int64_t(1) << 31))
+    return Q8_ERR_SHAPE;
   if (R == 0) return Q8_OK;
   if (codes == nullptr || scales == nullptr || out == nullptr) return Q8_ERR_NULL;
-  const int64_t esize = out_dtype == Q8_F32 ? 4 : 2;
-  if (!aligned(out, 16) || (ldo * esize) % 16 != 0 || !aligned(scales, 4)) return Q8_ERR_ALIGN;
+  if (!aligned(out, 16) || (ldo * esize) % 16 != 0 || !aligned(codes, 16) || !aligned(scales, 4))
+    return Q8_ERR_ALIGN;
   const q8_status dev = check_device();
   if (dev != Q8_OK) return dev;
   return q8::launch_kv3_decode(codes, scales, R, D, static_cast<int>(out_dtype), out, ldo,

@@ -158,6 +158,8 @@ def test_kv3_encode_validation(L):
     assert f(FAKE, 0, -1, 128, 128, FAKE, FAKE, None) == SHAPE
     assert f(FAKE, 0, 8, 128, 120, FAKE, FAKE, None) == SHAPE
     assert f(FAKE, 0, 1 << 34, 128, 128, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 0, 8, 128, 1 << 23, FAKE, FAKE, None) == SHAPE    # pitch 32 MiB
+    assert f(FAKE, 1, 8, 128, 1 << 24, FAKE, FAKE, None) == SHAPE
     assert f(None, 0, 0, 128, 128, None, None, None) == OK        # R == 0: no-op
     for i in (0, 5, 6):
         args = [FAKE, 0, 8, 128, 128, FAKE, FAKE]
@@ -167,9 +169,7 @@ def test_kv3_encode_validation(L):
     assert f(FAKE, 0, 8, 128, 130, FAKE, FAKE, None) == ALIGN      # 520-byte pitch
     assert f(FAKE, 1, 8, 128, 132, FAKE, FAKE, None) == ALIGN      # 264-byte pitch
     assert f(FAKE, 0, 8, 128, 128, FAKE, ODD, None) == ALIGN
-    # codes: any alignment, so an odd codes pointer is not an alignment error
-    # (the call then reaches the device check, which fails without a GPU)
-    assert f(FAKE, 0, 8, 128, 128, ODD, FAKE, None) not in (NULL, SHAPE, ALIGN, DTYPE)
+    assert f(FAKE, 0, 8, 128, 128, ctypes.c_void_p(0x10008), FAKE, None) == ALIGN
 
 
 def test_kv3_decode_validation(L):
@@ -180,6 +180,7 @@ def test_kv3_decode_validation(L):
         assert f(FAKE, FAKE, 8, D, 0, FAKE, 512, None) == SHAPE
     assert f(FAKE, FAKE, -2, 128, 0, FAKE, 128, None) == SHAPE
     assert f(FAKE, FAKE, 8, 256, 0, FAKE, 128, None) == SHAPE
+    assert f(FAKE, FAKE, 8, 128, 0, FAKE, 1 << 23, None) == SHAPE
     assert f(None, None, 0, 64, 0, None, 64, None) == OK
     for i in (0, 1, 5):
         args = [FAKE, FAKE, 8, 128, 0, FAKE, 128]
@@ -188,6 +189,7 @@ def test_kv3_decode_validation(L):
     assert f(FAKE, FAKE, 8, 128, 0, ODD, 128, None) == ALIGN
     assert f(FAKE, FAKE, 8, 128, 1, FAKE, 132, None) == ALIGN
     assert f(FAKE, ODD, 8, 128, 0, FAKE, 128, None) == ALIGN
+    assert f(ctypes.c_void_p(0x10004), FAKE, 8, 128, 0, FAKE, 128, None) == ALIGN
 
 
 def test_binding_refuses_cpu_tensors():
