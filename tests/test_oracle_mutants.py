@@ -48,6 +48,10 @@ MUTANTS = {
     "kv3_pack_stride": ("w |= (uint32_t)c << (3 * j);", "w |= (uint32_t)c << (3 * (7 - j));"),
     "kv3_decode_norm": ("out[r * D + i] = z[i] * (1.0f / (float)D);", "out[r * D + i] = z[i];"),
     "kv3_level_value": ("0.2451f,  0.7560f,", "0.2451f,  0.7650f,"),
+    "kv3_sum_drops_term": ("for (int i = 0; i < D; i += 2 * len) v[i] = v[i] + v[i + len];",
+                           "for (int i = 0; i < D; i += 2 * len) v[i] = v[i];"),
+    "kv3_sum_not_squared": ("for (int i = 0; i < D; ++i) v[i] = y[i] * y[i];",
+                            "for (int i = 0; i < D; ++i) v[i] = y[i];"),
 }
 
 
