@@ -60,6 +60,14 @@ def _bind(L):
     L.q8ref_kv3_encode.restype = None
     L.q8ref_kv3_decode.argtypes = [vp, vp, i64, ctypes.c_int, vp]
     L.q8ref_kv3_decode.restype = None
+    L.q8ref_attn_pool.argtypes = [vp, i64, i64, i64, ctypes.c_int, vp]
+    L.q8ref_attn_pool.restype = None
+    L.q8ref_attn_select.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, vp, vp]
+    L.q8ref_attn_select.restype = None
+    L.q8ref_attn_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int, vp, vp,
+                                 ctypes.c_int, vp, vp]
+    L.q8ref_attn_fwd.restype = None
     L.q8ref_num_threads.argtypes = []
     L.q8ref_num_threads.restype = ctypes.c_int
     return L
@@ -250,6 +258,45 @@ class Oracle:
         out = np.empty((R, D), dtype=np.float32)
         self.L.q8ref_kv3_decode(_p(codes), _p(scales), R, D, _p(out))
         return out
+
+    # -- block-sparse causal attention (64-token blocks) -------------------
+    ATTN_BLK = 64
+
+    def attn_pool(self, x, H, D):
+        """x: [L][>=H*D] uint16 bfloat16 bits, token-major -> pooled
+        [H][NB][D] float64, the mean of each 64-token block (the last block
+        may be shorter)."""
+        x = _c(x, np.uint16)
+        L, ldx = x.shape
+        NB = (L + 63) // 64
+        out = np.empty((H, NB, D), dtype=np.float64)
+        self.L.q8ref_attn_pool(_p(x), L, ldx, H, D, _p(out))
+        return out
+
+    def attn_select(self, pq, pk, k, kmax=None):
+        """Pooled rows ([Hq][NB][D], [Hkv][NB][D]) -> (idx int32
+        [Hq][NB][kmax], cnt int32 [Hq][NB]): block 0, the diagonal block and
+        the top-scoring others, ascending, -1 past cnt."""
+        pq, pk = _c(pq, np.float64), _c(pk, np.float64)
+        Hq, NB, D = pq.shape
+        Hkv = pk.shape[0]
+        kmax = k if kmax is None else kmax
+        idx = np.empty((Hq, NB, kmax), dtype=np.int32)
+        cnt = np.empty((Hq, NB), dtype=np.int32)
+        self.L.q8ref_attn_select(_p(pq), _p(pk), Hq, Hkv, NB, D, k, kmax, _p(idx), _p(cnt))
+        return idx, cnt
+
+    def attn_fwd(self, q, k, v, Hq, Hkv, D, idx, cnt):
+        """q [L][>=Hq*D], k, v [L][>=Hkv*D] uint16 bfloat16 bits; idx/cnt as
+        from attn_select -> (out, mag) float64 [L][Hq*D]."""
+        q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+        idx, cnt = _c(idx, np.int32), _c(cnt, np.int32)
+        L = q.shape[0]
+        out = np.empty((L, Hq * D), dtype=np.float64)
+        mag = np.empty((L, Hq * D), dtype=np.float64)
+        self.L.q8ref_attn_fwd(_p(q), _p(k), _p(v), L, q.shape[1], k.shape[1], v.shape[1], Hq, Hkv,
+                              D, _p(idx), _p(cnt), idx.shape[2], _p(out), _p(mag))
+        return out, mag
 
     def num_threads(self) -> int:
         return int(self.L.q8ref_num_threads())

@@ -468,6 +468,135 @@ void q8ref_kv3_decode(const uint8_t *codes, const float *scales, int64_t R, int 
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Block-sparse causal attention, prefill (the pages' "own FlashAttention + */
+/* MInference-style block-sparse"; nothing more is given, so the reading   */
+/* below is the plainest one, written from its description in the library */
+/* header):                                                                 */
+/*   Q [L][ldq], K [L][ldk], V [L][ldv] bfloat16, token-major; head h of Q  */
+/*   at columns h*D .. h*D+D-1, its K/V head g = h / (Hq/Hkv) likewise.     */
+/*   Blocks of 64 tokens; block i holds tokens 64i .. min(64i+63, L-1).     */
+/*   Pooled rows: the mean over a block's tokens of Q (per query head) and  */
+/*   of K (per K/V head).                                                   */
+/*   Selection: query block i of head h keeps block 0, block i, and the     */
+/*   top (k - 2) blocks 0 < j < i by score q_i . k_j of the pooled rows     */
+/*   (ties: lower j first); all blocks j <= i when k >= i + 1.  Listed in   */
+/*   ascending order, cnt = min(k, i + 1).                                  */
+/*   Output: token t of query block i attends to the keys u <= t of its     */
+/*   listed blocks: o = sum_u p_u v_u / sum_u p_u, p_u = exp(q.k_u / sqrt D */
+/*   - max), computed in double.                                            */
+/* ------------------------------------------------------------------------ */
+
+#define ATTN_BLK 64
+
+static double bf16d(const uint16_t *p) { return (double)q8ref_bf16_to_f32(*p); }
+
+/* pooled [H][NB][D] (double): mean over each block's tokens of x's head h. */
+void q8ref_attn_pool(const uint16_t *x, int64_t L, int64_t ldx, int64_t H, int D,
+                     double *pooled)
+{
+    const int64_t NB = (L + ATTN_BLK - 1) / ATTN_BLK;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t h = 0; h < H; ++h)
+        for (int64_t b = 0; b < NB; ++b) {
+            const int64_t t0 = b * ATTN_BLK, t1 = t0 + ATTN_BLK < L ? t0 + ATTN_BLK : L;
+            double *out = pooled + (h * NB + b) * D;
+            for (int d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int64_t t = t0; t < t1; ++t) acc += bf16d(x + t * ldx + h * D + d);
+                out[d] = acc / (double)(t1 - t0);
+            }
+        }
+}
+
+/* idx [Hq][NB][kmax] (ascending, the rest -1), cnt [Hq][NB]; k <= kmax. */
+void q8ref_attn_select(const double *pq, const double *pk, int64_t Hq, int64_t Hkv, int64_t NB,
+                       int D, int k, int kmax, int32_t *idx, int32_t *cnt)
+{
+    const int64_t group = Hq / Hkv;
+    #pragma omp parallel for collapse(2) schedule(dynamic, 16)
+    for (int64_t h = 0; h < Hq; ++h)
+        for (int64_t i = 0; i < NB; ++i) {
+            int32_t *row = idx + (h * NB + i) * kmax;
+            for (int m = 0; m < kmax; ++m) row[m] = -1;
+            char *take = calloc((size_t)i + 1, 1);
+            int n = 0;
+            if (k >= i + 1) {
+                for (int64_t j = 0; j <= i; ++j) take[j] = 1;
+                n = (int)i + 1;
+            } else {
+                take[0] = 1;
+                take[i] = 1;
+                n = i > 0 ? 2 : 1;
+                const double *q = pq + (h * NB + i) * D;
+                while (n < k) {                          /* next best: highest score, lowest j */
+                    int64_t best = -1;
+                    double bs = 0.0;
+                    for (int64_t j = 1; j < i; ++j) {
+                        if (take[j]) continue;
+                        const double *kk = pk + ((h / group) * NB + j) * D;
+                        double sc = 0.0;
+                        for (int d = 0; d < D; ++d) sc += q[d] * kk[d];
+                        if (best < 0 || sc > bs) { best = j; bs = sc; }
+                    }
+                    take[best] = 1;
+                    ++n;
+                }
+            }
+            int m = 0;
+            for (int64_t j = 0; j <= i; ++j)
+                if (take[j]) row[m++] = (int32_t)j;
+            cnt[h * NB + i] = n;
+            free(take);
+        }
+}
+
+/* out [L][Hq*D] and mag [L][Hq*D] (double): the attention output and, per
+ * element, sum_u p_u |v_u| / sum_u p_u (the scale of its rounding error). */
+void q8ref_attn_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int64_t L,
+                    int64_t ldq, int64_t ldk, int64_t ldv, int64_t Hq, int64_t Hkv, int D,
+                    const int32_t *idx, const int32_t *cnt, int kmax, double *out, double *mag)
+{
+    const int64_t NB = (L + ATTN_BLK - 1) / ATTN_BLK, group = Hq / Hkv;
+    const double scale = 1.0 / sqrt((double)D);
+    #pragma omp parallel for collapse(2) schedule(dynamic, 8)
+    for (int64_t h = 0; h < Hq; ++h)
+        for (int64_t t = 0; t < L; ++t) {
+            const int64_t i = t / ATTN_BLK, g = h / group;
+            const int32_t *row = idx + (h * NB + i) * kmax;
+            const int n = cnt[h * NB + i];
+            double *s = malloc(sizeof(double) * (size_t)n * ATTN_BLK);
+            int64_t *u_of = malloc(sizeof(int64_t) * (size_t)n * ATTN_BLK);
+            int ns = 0;
+            double mx = -INFINITY;
+            for (int m = 0; m < n; ++m)
+                for (int64_t u = (int64_t)row[m] * ATTN_BLK; u < ((int64_t)row[m] + 1) * ATTN_BLK; ++u) {
+                    if (u > t || u >= L) continue;
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dot += bf16d(Q + t * ldq + h * D + d) * bf16d(K + u * ldk + g * D + d);
+                    s[ns] = dot * scale;
+                    u_of[ns] = u;
+                    if (s[ns] > mx) mx = s[ns];
+                    ++ns;
+                }
+            double den = 0.0;
+            for (int a = 0; a < ns; ++a) { s[a] = exp(s[a] - mx); den += s[a]; }
+            for (int d = 0; d < D; ++d) {
+                double num = 0.0, am = 0.0;
+                for (int a = 0; a < ns; ++a) {
+                    const double v = bf16d(V + u_of[a] * ldv + g * D + d);
+                    num += s[a] * v;
+                    am += s[a] * fabs(v);
+                }
+                out[t * Hq * D + h * D + d] = num / den;
+                mag[t * Hq * D + h * D + d] = am / den;
+            }
+            free(s);
+            free(u_of);
+        }
+}
+
 /* Threads the OpenMP runtime will use (for reporting the CPU baseline). */
 int q8ref_num_threads(void)
 {

@@ -555,8 +555,147 @@ def pin_kv3_roundtrip(orc):
     assert np.array_equal(ca, cb) and np.array_equal(sa, sb)
 
 
+# -- block-sparse causal attention --------------------------------------
+
+def _bf16(a):
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _widen(b):
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _attn_inputs(L, Hq, Hkv, D, seed):
+    r = np.random.default_rng(seed)
+    q = _bf16(r.standard_normal((L, Hq * D)))
+    k = _bf16(r.standard_normal((L, Hkv * D)))
+    v = _bf16(r.standard_normal((L, Hkv * D)))
+    return q, k, v
+
+
+def _sdpa(q, k, v, Hq, Hkv, D, allowed):
+    """torch's float64 scaled_dot_product_attention; allowed [Hq][L][L] bool
+    (query t may attend key u)."""
+    import torch
+    L = q.shape[0]
+    Q = torch.from_numpy(_widen(q).reshape(L, Hq, D).transpose(1, 0, 2).copy())
+    K = torch.from_numpy(_widen(k).reshape(L, Hkv, D).transpose(1, 0, 2).copy())
+    V = torch.from_numpy(_widen(v).reshape(L, Hkv, D).transpose(1, 0, 2).copy())
+    K = K.repeat_interleave(Hq // Hkv, dim=0)
+    V = V.repeat_interleave(Hq // Hkv, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        Q[None], K[None], V[None], attn_mask=torch.from_numpy(allowed)[None])
+    return o[0].numpy().transpose(1, 0, 2).reshape(L, Hq * D)
+
+
+def _allowed_from_lists(idx, cnt, L):
+    Hq, NB, _ = idx.shape
+    allowed = np.zeros((Hq, L, L), dtype=bool)
+    for h in range(Hq):
+        for i in range(NB):
+            for j in idx[h, i, :cnt[h, i]]:
+                allowed[h, 64 * i:64 * i + 64, 64 * j:64 * j + 64] = True
+    return allowed & np.tril(np.ones((L, L), dtype=bool))[None]
+
+
+def pin_attn_dense(orc):
+    """With every block listed, block-sparse attention is dense causal
+    attention: torch's scaled_dot_product_attention in float64 (grouped
+    query heads expanded by repetition), ragged L."""
+    for L, Hq, Hkv, D in ((200, 4, 2, 64), (130, 2, 1, 128)):
+        q, k, v = _attn_inputs(L, Hq, Hkv, D, L + D)
+        NB = (L + 63) // 64
+        idx, cnt = orc.attn_select(orc.attn_pool(q, Hq, D), orc.attn_pool(k, Hkv, D), NB)
+        out, mag = orc.attn_fwd(q, k, v, Hq, Hkv, D, idx, cnt)
+        ref = _sdpa(q, k, v, Hq, Hkv, D, np.broadcast_to(np.tril(np.ones((L, L), bool)), (Hq, L, L)).copy())
+        assert np.max(np.abs(out - ref)) < 1e-12, np.max(np.abs(out - ref))
+        assert np.all(mag >= np.abs(out) - 1e-12)
+
+
+def pin_attn_masked(orc):
+    """Arbitrary block lists (block 0 and the diagonal always present):
+    the output is torch's attention under the block-and-causal mask."""
+    L, Hq, Hkv, D = 330, 4, 2, 64
+    q, k, v = _attn_inputs(L, Hq, Hkv, D, 7)
+    NB = (L + 63) // 64
+    r = np.random.default_rng(8)
+    kmax = 4
+    idx = np.full((Hq, NB, kmax), -1, np.int32)
+    cnt = np.zeros((Hq, NB), np.int32)
+    for h in range(Hq):
+        for i in range(NB):
+            extra = [j for j in range(1, i) if r.random() < 0.4][:kmax - 2]
+            blocks = sorted(set([0, i] + extra))
+            idx[h, i, :len(blocks)] = blocks
+            cnt[h, i] = len(blocks)
+    out, _ = orc.attn_fwd(q, k, v, Hq, Hkv, D, idx, cnt)
+    ref = _sdpa(q, k, v, Hq, Hkv, D, _allowed_from_lists(idx, cnt, L))
+    assert np.max(np.abs(out - ref)) < 1e-12, np.max(np.abs(out - ref))
+
+
+def pin_attn_invariants(orc):
+    """Constant value rows give that constant; the first token sees only
+    itself, so its output is its own value row; outputs are convex
+    combinations (within [min v, max v] per column)."""
+    L, Hq, Hkv, D = 150, 2, 2, 64
+    q, k, v = _attn_inputs(L, Hq, Hkv, D, 11)
+    pq, pk = orc.attn_pool(q, Hq, D), orc.attn_pool(k, Hkv, D)
+    idx, cnt = orc.attn_select(pq, pk, 2)
+    out, _ = orc.attn_fwd(q, k, v, Hq, Hkv, D, idx, cnt)
+    assert np.array_equal(out[0], _widen(v[0]))
+    vw = _widen(v).reshape(L, Hkv, D)
+    o = out.reshape(L, Hq, D)
+    assert np.all(o <= vw.max(axis=0)[None] + 1e-12) and np.all(o >= vw.min(axis=0)[None] - 1e-12)
+    c = _bf16(np.tile(np.linspace(-3, 3, Hkv * D), (L, 1)))
+    out_c, _ = orc.attn_fwd(q, k, c, Hq, Hkv, D, idx, cnt)
+    assert np.max(np.abs(out_c - np.tile(_widen(c[0]), (L, 1)).reshape(L, Hkv, D).repeat(Hq // Hkv, axis=1).reshape(L, -1))) < 1e-14
+
+
+def pin_attn_pool(orc):
+    """Pooled rows are numpy's means over each block's tokens (a shorter
+    last block included)."""
+    L, H, D = 170, 3, 64
+    x = _bf16(np.random.default_rng(3).standard_normal((L, H * D)))
+    p = orc.attn_pool(x, H, D)
+    w = _widen(x).reshape(L, H, D)
+    for b in range(3):
+        assert np.allclose(p[:, b], w[64 * b:64 * b + 64].mean(axis=0), rtol=0, atol=1e-15)
+
+
+def pin_attn_select(orc):
+    """Selection rules, and a planted ranking: K rows of block j all equal
+    c_j e_0 and Q rows equal e_0, so the score of block j is c_j; the kept
+    blocks are 0, i and the (k-2) largest c_j among 0 < j < i, the lower j
+    first on equal c_j."""
+    D, NB = 64, 12
+    L = 64 * NB
+    c = np.array([0.5, 3, 1, 3, 2, 0.25, 3, 1.5, 0.75, 2, 1, 0.125])   # per key block
+    q = np.zeros((L, D), np.float32)
+    q[:, 0] = 1.0
+    kk = np.zeros((L, D), np.float32)
+    for j in range(NB):
+        kk[64 * j:64 * j + 64, 0] = c[j]
+    pq, pk = orc.attn_pool(_bf16(q), 1, D), orc.attn_pool(_bf16(kk), 1, D)
+    for k in (2, 3, 4, 5):
+        idx, cnt = orc.attn_select(pq, pk, k)
+        for i in range(NB):
+            got = list(idx[0, i, :cnt[0, i]])
+            assert cnt[0, i] == min(k, i + 1) and got == sorted(set(got)), (k, i, got)
+            assert all(j <= i for j in got) and (0 in got) and (i in got)
+            if k >= i + 1:
+                assert got == list(range(i + 1))
+                continue
+            others = sorted(range(1, i), key=lambda j: (-c[j], j))[:k - 2]
+            assert got == sorted(set([0, i] + others)), (k, i, got, others)
+    # hand check of one row: i = 9, k = 4: scores 3 (j=1), 3 (3), 3 (6): keep 1, 3
+    idx, cnt = orc.attn_select(pq, pk, 4)
+    assert list(idx[0, 9, :4]) == [0, 1, 3, 9]
+
+
 ALL_PINS = [pin_f16_roundtrip_all, pin_f16_vs_numpy, pin_quant_golden, pin_quant_exact_random,
             pin_quant_invariants, pin_quant_rows, pin_gemm_golden, pin_gemm_exact,
             pin_gemm_unit_scale, pin_block_dots, pin_gemm_sampled, pin_block_bytes,
             pin_pack_layout, pin_silu, pin_swiglu_golden, pin_swiglu_rows, pin_gateup_layout,
-            pin_kv3_codebook, pin_fwht, pin_kv3_golden, pin_kv3_code_positions, pin_kv3_roundtrip]
+            pin_kv3_codebook, pin_fwht, pin_kv3_golden, pin_kv3_code_positions, pin_kv3_roundtrip,
+            pin_attn_dense, pin_attn_masked, pin_attn_invariants, pin_attn_pool, pin_attn_select]

@@ -50,6 +50,16 @@ MUTANTS = {
     "kv3_level_value": ("0.2451f,  0.7560f,", "0.2451f,  0.7650f,"),
     "kv3_sum_drops_term": ("for (int i = 0; i < D; i += 2 * len) v[i] = v[i] + v[i + len];",
                            "for (int i = 0; i < D; i += 2 * len) v[i] = v[i];"),
+    "attn_not_causal": ("if (u > t || u >= L) continue;", "if (u >= L) continue;"),
+    "attn_scale_no_sqrt": ("const double scale = 1.0 / sqrt((double)D);",
+                           "const double scale = 1.0 / (double)D;"),
+    "attn_gqa_mapping": ("const int64_t i = t / ATTN_BLK, g = h / group;",
+                         "const int64_t i = t / ATTN_BLK, g = h % Hkv;"),
+    "attn_no_sink": ("                take[0] = 1;\n", "                take[1 < i ? 1 : 0] = 1;\n"),
+    "attn_ties_high": ("if (best < 0 || sc > bs) { best = j; bs = sc; }",
+                       "if (best < 0 || sc >= bs) { best = j; bs = sc; }"),
+    "attn_pool_divisor": ("out[d] = acc / (double)(t1 - t0);", "out[d] = acc / (double)ATTN_BLK;"),
+    "attn_diag_block_dropped": ("                take[i] = 1;\n", "                take[i - 1] = 1;\n"),
     "kv3_sum_not_squared": ("for (int i = 0; i < D; ++i) v[i] = y[i] * y[i];",
                             "for (int i = 0; i < D; ++i) v[i] = y[i];"),
 }
