@@ -279,6 +279,61 @@ q8_status q8_kv3_encode(const void *x, q8_dtype dtype, int64_t R, int64_t D, int
 q8_status q8_kv3_decode(const uint8_t *codes, const float *scales, int64_t R, int64_t D,
                         q8_dtype out_dtype, void *out, int64_t ldo, void *stream);
 
+/*
+ * Block-sparse causal attention for long-context prefill: q8_attn_pool,
+ * q8_attn_select, q8_attn_fwd.
+ *
+ * Source: the source engine computes attention with its own FlashAttention
+ * kernel and MInference-style block sparsity (news.hada.io topic 29953,
+ * list of paths that avoid the throttled units, attention item).  The pages
+ * say no more; the operation below is this library's reading of it.
+ *
+ * Tokens form blocks of 64 (block b: tokens 64b .. min(64b+63, L-1)).
+ * Q [L][ldq], K [L][ldk], V [L][ldv] are bfloat16, token-major: query head
+ * h occupies columns h*D .. h*D+D-1 of Q, and reads key/value head
+ * g = h / (Hq/Hkv) at columns g*D .. of K and V (grouped-query heads).
+ *
+ * q8_attn_pool: pooled[h][b][d] (binary32) = mean over block b's tokens of
+ *   x[t][h*D + d].  x is Q (H = Hq) or K (H = Hkv).  pooled has
+ *   H * NB * D floats, NB = ceil(L/64), and is 16-byte aligned.
+ *   x: 16-byte aligned, ldx >= H*D, ldx*2 % 16 == 0, ldx < 2^24.
+ *
+ * q8_attn_select: for every query head h and query block i, the key blocks
+ *   it attends to: block 0, block i, and the k - 2 blocks 0 < j < i with the
+ *   highest score pooled_q[h][i] . pooled_k[g][j] (higher score first, the
+ *   lower j on equal scores); every block j <= i when k >= i + 1.
+ *   idx [Hq][NB][kmax] int32 receives them in ascending order, -1 after the
+ *   last; cnt [Hq][NB] int32 receives min(k, i + 1).  2 <= k <= kmax,
+ *   NB <= 4096.  Scores are binary32 dot products of the binary32 pooled
+ *   rows; blocks whose scores differ from the k-2'th by a few binary32
+ *   units may be chosen either way.
+ *
+ * q8_attn_fwd: out[t][h*D + d] = sum_u p_u V[u][g*D + d] / sum_u p_u over
+ *   the keys u <= t of the blocks listed for t's block (idx/cnt as written by
+ *   q8_attn_select, or any list of blocks 0 <= j <= i in ascending order),
+ *   p_u = exp(q_t . k_u / sqrt(D) - max).  Scores and sums in binary32 on
+ *   the bf16 matrix cores, p rounded to bfloat16 for the product with V (as
+ *   in FlashAttention), so |out - exact| <= ~2^-8 * sum_u p_u |V_u| / sum_u p_u
+ *   (plus the output's rounding for bfloat16).  List entries outside
+ *   [0, i] are skipped and cnt is clamped to [0, kmax]; an empty list gives
+ *   non-finite output.  out: out_dtype Q8_F32 (16-byte aligned,
+ *   ldo*4 % 16 == 0) or Q8_BF16 (8-byte aligned, ldo*2 % 8 == 0), ldo >= Hq*D.
+ *   Q, K, V: 16-byte aligned, ld*2 % 16 == 0, ld >= heads*D, ld < 2^24.
+ *   D = 64 or 128; Hq % Hkv == 0; L <= 262144.
+ *
+ * Errors (all three): Q8_ERR_NULL, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DTYPE
+ * (q8_attn_fwd), Q8_ERR_DEVICE, Q8_ERR_LAUNCH.  L == 0 (NB == 0) is a no-op.
+ */
+q8_status q8_attn_pool(const void *x, int64_t L, int64_t ldx, int64_t H, int64_t D,
+                       float *pooled, void *stream);
+q8_status q8_attn_select(const float *pooled_q, const float *pooled_k, int64_t Hq, int64_t Hkv,
+                         int64_t NB, int64_t D, int k, int kmax, int32_t *idx, int32_t *cnt,
+                         void *stream);
+q8_status q8_attn_fwd(const void *q, const void *k, const void *v, int64_t L, int64_t ldq,
+                      int64_t ldk, int64_t ldv, int64_t Hq, int64_t Hkv, int64_t D,
+                      const int32_t *idx, const int32_t *cnt, int kmax, q8_dtype out_dtype,
+                      void *out, int64_t ldo, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *q8_status_string(q8_status s);
 

@@ -28,7 +28,7 @@ STATUS = {0: "Q8_OK", 1: "Q8_ERR_NULL", 2: "Q8_ERR_SHAPE", 3: "Q8_ERR_ALIGN",
           4: "Q8_ERR_DTYPE", 5: "Q8_ERR_SIZE", 6: "Q8_ERR_DEVICE", 7: "Q8_ERR_LAUNCH"}
 EXPORTS = ("q8_pack_weights", "q8_quantize_act", "q8_gemm", "q8_gemm_act",
            "q8_pack_weights_gateup", "q8_gemm_swiglu", "q8_kv3_encode", "q8_kv3_decode",
-           "q8_status_string")
+           "q8_attn_pool", "q8_attn_select", "q8_attn_fwd", "q8_status_string")
 
 _lib = None
 
@@ -66,6 +66,14 @@ def _load():
         L.q8_kv3_encode.restype = ctypes.c_int
         L.q8_kv3_decode.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp, i64, vp]
         L.q8_kv3_decode.restype = ctypes.c_int
+        L.q8_attn_pool.argtypes = [vp, i64, i64, i64, i64, vp, vp]
+        L.q8_attn_pool.restype = ctypes.c_int
+        L.q8_attn_select.argtypes = [vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp,
+                                     vp]
+        L.q8_attn_select.restype = ctypes.c_int
+        L.q8_attn_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp, vp,
+                                  ctypes.c_int, ctypes.c_int, vp, i64, vp]
+        L.q8_attn_fwd.restype = ctypes.c_int
         L.q8_status_string.argtypes = [ctypes.c_int]
         L.q8_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -303,4 +311,69 @@ def q8_kv3_decode(codes: torch.Tensor, scales: torch.Tensor, D: int,
     ldo = out.stride(0) if R > 1 else max(out.stride(0), D)
     _check("q8_kv3_decode", _load().q8_kv3_decode(
         _ptr(codes), _ptr(scales), R, D, odt, _ptr(out), ldo, _stream(codes)))
+    return out
+
+
+def _bf16_rows(name, t):
+    _need_cuda(name, t)
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1:
+        raise TypeError("%s must be 2-D bfloat16 with unit column stride" % name)
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def q8_attn_pool(x: torch.Tensor, H: int, D: int, out: torch.Tensor = None) -> torch.Tensor:
+    """Token-major bfloat16 rows x [L][>=H*D] -> pooled block means float32
+    [H][ceil(L/64)][D]."""
+    ldx = _bf16_rows("x", x)
+    L = x.shape[0]
+    NB = (L + 63) // 64
+    if out is None:
+        out = torch.empty((H, NB, D), dtype=torch.float32, device=x.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (H, NB, D):
+        raise TypeError("out must be contiguous float32 [H][NB][D]")
+    _check("q8_attn_pool", _load().q8_attn_pool(_ptr(x), L, ldx, H, D, _ptr(out), _stream(x)))
+    return out
+
+
+def q8_attn_select(pooled_q: torch.Tensor, pooled_k: torch.Tensor, k: int, kmax: int = None,
+                   idx: torch.Tensor = None, cnt: torch.Tensor = None):
+    """Pooled rows [Hq][NB][D], [Hkv][NB][D] -> (idx int32 [Hq][NB][kmax],
+    cnt int32 [Hq][NB]): the key blocks of every query block."""
+    for name, t in (("pooled_q", pooled_q), ("pooled_k", pooled_k)):
+        _need_cuda(name, t)
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 3:
+            raise TypeError("%s must be contiguous float32 [H][NB][D]" % name)
+    Hq, NB, D = pooled_q.shape
+    Hkv = pooled_k.shape[0]
+    kmax = k if kmax is None else kmax
+    if idx is None:
+        idx = torch.empty((Hq, NB, kmax), dtype=torch.int32, device=pooled_q.device)
+    if cnt is None:
+        cnt = torch.empty((Hq, NB), dtype=torch.int32, device=pooled_q.device)
+    _check("q8_attn_select", _load().q8_attn_select(_ptr(pooled_q), _ptr(pooled_k), Hq, Hkv, NB, D,
+                                                    k, kmax, _ptr(idx), _ptr(cnt),
+                                                    _stream(pooled_q)))
+    return idx, cnt
+
+
+def q8_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, Hq: int, Hkv: int, D: int,
+                idx: torch.Tensor, cnt: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                out: torch.Tensor = None) -> torch.Tensor:
+    """Block-sparse causal attention over the listed key blocks: q [L][>=Hq*D],
+    k, v [L][>=Hkv*D] bfloat16 -> out [L][Hq*D] (bfloat16 or float32)."""
+    ldq, ldk, ldv = _bf16_rows("q", q), _bf16_rows("k", k), _bf16_rows("v", v)
+    for name, t in (("idx", idx), ("cnt", cnt)):
+        _need_cuda(name, t)
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError("%s must be contiguous int32" % name)
+    L = q.shape[0]
+    if out is None:
+        out = torch.empty((L, Hq * D), dtype=out_dtype, device=q.device)
+    odt = _act_dtype(out)
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != L or out.shape[1] < Hq * D:
+        raise TypeError("out must be [L][>=Hq*D] with unit column stride")
+    ldo = out.stride(0) if L > 1 else out.shape[1]
+    _check("q8_attn_fwd", _load().q8_attn_fwd(_ptr(q), _ptr(k), _ptr(v), L, ldq, ldk, ldv, Hq, Hkv,
+                                              D, _ptr(idx), _ptr(cnt), idx.shape[-1], odt,
+                                              _ptr(out), ldo, _stream(q)))
     return out

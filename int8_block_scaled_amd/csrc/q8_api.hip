@@ -38,6 +38,12 @@ constexpr int64_t kMaxK = int64_t(1) << 24;
 bool valid_k(int64_t K) { return K >= 32 && K % 32 == 0 && K <= kMaxK; }
 
 bool valid_head_dim(int64_t D) { return D == 64 || D == 128 || D == 256; }
+bool valid_attn_dim(int64_t D) { return D == 64 || D == 128; }
+// attention: 64-token blocks, at most 4096 of them (262144 tokens); row
+// pitches below 2^24 elements, so that 64 rows of a block fit a 32-bit
+// buffer range
+constexpr int64_t kMaxAttnBlocks = 4096;
+constexpr int64_t kMaxAttnLd = int64_t(1) << 24;
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -229,6 +235,71 @@ q8_status q8_kv3_decode(const uint8_t* codes, const float* scales, int64_t R, in
   if (dev != Q8_OK) return dev;
   return q8::launch_kv3_decode(codes, scales, R, D, static_cast<int>(out_dtype), out, ldo,
                                as_stream(stream)) == hipSuccess
+             ? Q8_OK
+             : Q8_ERR_LAUNCH;
+}
+
+q8_status q8_attn_pool(const void* x, int64_t L, int64_t ldx, int64_t H, int64_t D, float* pooled,
+                       void* stream) {
+  if (L < 0 || H < 1 || !valid_attn_dim(D) || ldx < H * D || ldx >= kMaxAttnLd) return Q8_ERR_SHAPE;
+  if (L == 0) return Q8_OK;
+  const int64_t NB = (L + 63) / 64;
+  if (NB > kMaxAttnBlocks || H * NB >= kMaxDim) return Q8_ERR_SHAPE;
+  if (x == nullptr || pooled == nullptr) return Q8_ERR_NULL;
+  if (!aligned(x, 16) || (ldx * 2) % 16 != 0 || !aligned(pooled, 16)) return Q8_ERR_ALIGN;
+  const q8_status dev = check_device();
+  if (dev != Q8_OK) return dev;
+  return q8::launch_attn_pool(static_cast<const uint16_t*>(x), L, ldx, H, D, pooled,
+                              as_stream(stream)) == hipSuccess
+             ? Q8_OK
+             : Q8_ERR_LAUNCH;
+}
+
+q8_status q8_attn_select(const float* pooled_q, const float* pooled_k, int64_t Hq, int64_t Hkv,
+                         int64_t NB, int64_t D, int k, int kmax, int32_t* idx, int32_t* cnt,
+                         void* stream) {
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || NB < 0 || NB > kMaxAttnBlocks || !valid_attn_dim(D) ||
+      k < 2 || kmax < k || Hq * NB >= kMaxDim)
+    return Q8_ERR_SHAPE;
+  if (NB == 0) return Q8_OK;
+  if (pooled_q == nullptr || pooled_k == nullptr || idx == nullptr || cnt == nullptr)
+    return Q8_ERR_NULL;
+  if (!aligned(pooled_q, 16) || !aligned(pooled_k, 16) || !aligned(idx, 4) || !aligned(cnt, 4))
+    return Q8_ERR_ALIGN;
+  const q8_status dev = check_device();
+  if (dev != Q8_OK) return dev;
+  return q8::launch_attn_select(pooled_q, pooled_k, Hq, Hkv, NB, D, k, kmax, idx, cnt,
+                                as_stream(stream)) == hipSuccess
+             ? Q8_OK
+             : Q8_ERR_LAUNCH;
+}
+
+q8_status q8_attn_fwd(const void* q, const void* k, const void* v, int64_t L, int64_t ldq,
+                      int64_t ldk, int64_t ldv, int64_t Hq, int64_t Hkv, int64_t D,
+                      const int32_t* idx, const int32_t* cnt, int kmax, q8_dtype out_dtype,
+                      void* out, int64_t ldo, void* stream) {
+  if (out_dtype != Q8_F32 && out_dtype != Q8_BF16) return Q8_ERR_DTYPE;
+  if (L < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !valid_attn_dim(D) || kmax < 1 ||
+      ldq < Hq * D || ldk < Hkv * D || ldv < Hkv * D || ldo < Hq * D || ldq >= kMaxAttnLd ||
+      ldk >= kMaxAttnLd || ldv >= kMaxAttnLd || ldo >= kMaxAttnLd)
+    return Q8_ERR_SHAPE;
+  if (L == 0) return Q8_OK;
+  const int64_t NB = (L + 63) / 64;
+  if (NB > kMaxAttnBlocks || Hq * NB >= kMaxDim) return Q8_ERR_SHAPE;
+  if (q == nullptr || k == nullptr || v == nullptr || idx == nullptr || cnt == nullptr ||
+      out == nullptr)
+    return Q8_ERR_NULL;
+  const int64_t oalign = out_dtype == Q8_F32 ? 16 : 8, osize = out_dtype == Q8_F32 ? 4 : 2;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || (ldq * 2) % 16 != 0 ||
+      (ldk * 2) % 16 != 0 || (ldv * 2) % 16 != 0 || !aligned(idx, 4) || !aligned(cnt, 4) ||
+      !aligned(out, static_cast<uintptr_t>(oalign)) || (ldo * osize) % oalign != 0)
+    return Q8_ERR_ALIGN;
+  const q8_status dev = check_device();
+  if (dev != Q8_OK) return dev;
+  return q8::launch_attn_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                             static_cast<const uint16_t*>(v), L, ldq, ldk, ldv, Hq, Hkv, D, idx, cnt,
+                             kmax, static_cast<int>(out_dtype), out, ldo, as_stream(stream)) ==
+                 hipSuccess
              ? Q8_OK
              : Q8_ERR_LAUNCH;
 }

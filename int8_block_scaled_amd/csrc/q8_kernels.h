@@ -45,6 +45,17 @@ hipError_t launch_gemv_act(int M, const void* x, int dtype, int64_t ldx, int64_t
                            const uint8_t* w_packed, float* C, int64_t ldc, int8_t* q_out,
                            uint16_t* d_out, hipStream_t stream);
 
+// Block-sparse causal attention (q8_attn.hip); D in {64, 128}, 64-token blocks.
+hipError_t launch_attn_pool(const uint16_t* x, int64_t L, int64_t ldx, int64_t H, int64_t D,
+                            float* pooled, hipStream_t stream);
+hipError_t launch_attn_select(const float* pq, const float* pk, int64_t Hq, int64_t Hkv, int64_t NB,
+                              int64_t D, int k, int kmax, int32_t* idx, int32_t* cnt,
+                              hipStream_t stream);
+hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t L,
+                           int64_t ldq, int64_t ldk, int64_t ldv, int64_t Hq, int64_t Hkv, int64_t D,
+                           const int32_t* idx, const int32_t* cnt, int kmax, int out_dtype,
+                           void* out, int64_t ldo, hipStream_t stream);
+
 // 3-bit KV-cache codec (q8_kv3.hip); D in {64, 128, 256}.
 hipError_t launch_kv3_encode(const void* x, int dtype, int64_t R, int64_t D, int64_t ldx,
                              uint8_t* codes, float* scales, hipStream_t stream);

@@ -68,6 +68,9 @@ def _bind(L):
     L.q8ref_attn_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int, vp, vp,
                                  ctypes.c_int, vp, vp]
     L.q8ref_attn_fwd.restype = None
+    L.q8ref_attn_fwd_at.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int, vp,
+                                    vp, ctypes.c_int, vp, vp, i64, vp, vp]
+    L.q8ref_attn_fwd_at.restype = None
     L.q8ref_num_threads.argtypes = []
     L.q8ref_num_threads.restype = ctypes.c_int
     return L
@@ -296,6 +299,19 @@ class Oracle:
         mag = np.empty((L, Hq * D), dtype=np.float64)
         self.L.q8ref_attn_fwd(_p(q), _p(k), _p(v), L, q.shape[1], k.shape[1], v.shape[1], Hq, Hkv,
                               D, _p(idx), _p(cnt), idx.shape[2], _p(out), _p(mag))
+        return out, mag
+
+    def attn_fwd_at(self, q, k, v, Hq, Hkv, D, idx, cnt, tok, head):
+        """attn_fwd at chosen (token, head) pairs -> (out, mag) [n][D]."""
+        q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+        idx, cnt = _c(idx, np.int32), _c(cnt, np.int32)
+        tok, head = _c(tok, np.int64), _c(head, np.int64)
+        n = tok.size
+        out = np.empty((n, D), dtype=np.float64)
+        mag = np.empty((n, D), dtype=np.float64)
+        self.L.q8ref_attn_fwd_at(_p(q), _p(k), _p(v), q.shape[0], q.shape[1], k.shape[1],
+                                 v.shape[1], Hq, Hkv, D, _p(idx), _p(cnt), idx.shape[2],
+                                 _p(tok), _p(head), n, _p(out), _p(mag))
         return out, mag
 
     def num_threads(self) -> int:

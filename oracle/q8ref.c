@@ -551,50 +551,71 @@ void q8ref_attn_select(const double *pq, const double *pk, int64_t Hq, int64_t H
         }
 }
 
+/* One output row: token t of query head h -> o[D], m[D] (double). */
+static void attn_row(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int64_t L,
+                     int64_t ldq, int64_t ldk, int64_t ldv, int64_t Hq, int64_t Hkv, int D,
+                     const int32_t *idx, const int32_t *cnt, int kmax, int64_t t, int64_t h,
+                     double *o, double *mg)
+{
+    const int64_t NB = (L + ATTN_BLK - 1) / ATTN_BLK, group = Hq / Hkv;
+    const double scale = 1.0 / sqrt((double)D);
+    const int64_t i = t / ATTN_BLK, g = h / group;
+    const int32_t *row = idx + (h * NB + i) * kmax;
+    const int n = cnt[h * NB + i];
+    double *s = malloc(sizeof(double) * (size_t)n * ATTN_BLK);
+    int64_t *u_of = malloc(sizeof(int64_t) * (size_t)n * ATTN_BLK);
+    int ns = 0;
+    double mx = -INFINITY;
+    for (int m = 0; m < n; ++m)
+        for (int64_t u = (int64_t)row[m] * ATTN_BLK; u < ((int64_t)row[m] + 1) * ATTN_BLK; ++u) {
+            if (u > t || u >= L) continue;
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d)
+                dot += bf16d(Q + t * ldq + h * D + d) * bf16d(K + u * ldk + g * D + d);
+            s[ns] = dot * scale;
+            u_of[ns] = u;
+            if (s[ns] > mx) mx = s[ns];
+            ++ns;
+        }
+    double den = 0.0;
+    for (int a = 0; a < ns; ++a) { s[a] = exp(s[a] - mx); den += s[a]; }
+    for (int d = 0; d < D; ++d) {
+        double num = 0.0, am = 0.0;
+        for (int a = 0; a < ns; ++a) {
+            const double v = bf16d(V + u_of[a] * ldv + g * D + d);
+            num += s[a] * v;
+            am += s[a] * fabs(v);
+        }
+        o[d] = num / den;
+        mg[d] = am / den;
+    }
+    free(s);
+    free(u_of);
+}
+
 /* out [L][Hq*D] and mag [L][Hq*D] (double): the attention output and, per
  * element, sum_u p_u |v_u| / sum_u p_u (the scale of its rounding error). */
 void q8ref_attn_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int64_t L,
                     int64_t ldq, int64_t ldk, int64_t ldv, int64_t Hq, int64_t Hkv, int D,
                     const int32_t *idx, const int32_t *cnt, int kmax, double *out, double *mag)
 {
-    const int64_t NB = (L + ATTN_BLK - 1) / ATTN_BLK, group = Hq / Hkv;
-    const double scale = 1.0 / sqrt((double)D);
     #pragma omp parallel for collapse(2) schedule(dynamic, 8)
     for (int64_t h = 0; h < Hq; ++h)
-        for (int64_t t = 0; t < L; ++t) {
-            const int64_t i = t / ATTN_BLK, g = h / group;
-            const int32_t *row = idx + (h * NB + i) * kmax;
-            const int n = cnt[h * NB + i];
-            double *s = malloc(sizeof(double) * (size_t)n * ATTN_BLK);
-            int64_t *u_of = malloc(sizeof(int64_t) * (size_t)n * ATTN_BLK);
-            int ns = 0;
-            double mx = -INFINITY;
-            for (int m = 0; m < n; ++m)
-                for (int64_t u = (int64_t)row[m] * ATTN_BLK; u < ((int64_t)row[m] + 1) * ATTN_BLK; ++u) {
-                    if (u > t || u >= L) continue;
-                    double dot = 0.0;
-                    for (int d = 0; d < D; ++d)
-                        dot += bf16d(Q + t * ldq + h * D + d) * bf16d(K + u * ldk + g * D + d);
-                    s[ns] = dot * scale;
-                    u_of[ns] = u;
-                    if (s[ns] > mx) mx = s[ns];
-                    ++ns;
-                }
-            double den = 0.0;
-            for (int a = 0; a < ns; ++a) { s[a] = exp(s[a] - mx); den += s[a]; }
-            for (int d = 0; d < D; ++d) {
-                double num = 0.0, am = 0.0;
-                for (int a = 0; a < ns; ++a) {
-                    const double v = bf16d(V + u_of[a] * ldv + g * D + d);
-                    num += s[a] * v;
-                    am += s[a] * fabs(v);
-                }
-                out[t * Hq * D + h * D + d] = num / den;
-                mag[t * Hq * D + h * D + d] = am / den;
-            }
-            free(s);
-            free(u_of);
-        }
+        for (int64_t t = 0; t < L; ++t)
+            attn_row(Q, K, V, L, ldq, ldk, ldv, Hq, Hkv, D, idx, cnt, kmax, t, h,
+                     out + t * Hq * D + h * D, mag + t * Hq * D + h * D);
+}
+
+/* The same at n chosen (token, head) pairs: out, mag [n][D]. */
+void q8ref_attn_fwd_at(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int64_t L,
+                       int64_t ldq, int64_t ldk, int64_t ldv, int64_t Hq, int64_t Hkv, int D,
+                       const int32_t *idx, const int32_t *cnt, int kmax, const int64_t *tok,
+                       const int64_t *head, int64_t n, double *out, double *mag)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t a = 0; a < n; ++a)
+        attn_row(Q, K, V, L, ldq, ldk, ldv, Hq, Hkv, D, idx, cnt, kmax, tok[a], head[a],
+                 out + a * D, mag + a * D);
 }
 
 /* Threads the OpenMP runtime will use (for reporting the CPU baseline). */

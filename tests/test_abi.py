@@ -192,6 +192,61 @@ def test_kv3_decode_validation(L):
     assert f(ctypes.c_void_p(0x10004), FAKE, 8, 128, 0, FAKE, 128, None) == ALIGN
 
 
+def test_attn_pool_validation(L):
+    f = L.q8_attn_pool
+    #          x   L    ldx  H  D   pooled
+    assert f(FAKE, 100, 512, 5, 128, FAKE, None) == SHAPE          # ldx < H*D
+    assert f(FAKE, 100, 512, 4, 96, FAKE, None) == SHAPE           # D not 64/128
+    assert f(FAKE, -1, 512, 4, 64, FAKE, None) == SHAPE
+    assert f(FAKE, 64 * 4097, 512, 4, 64, FAKE, None) == SHAPE     # > 4096 blocks
+    assert f(None, 0, 512, 4, 64, None, None) == OK                # L == 0
+    assert f(None, 100, 512, 4, 64, FAKE, None) == NULL
+    assert f(ODD, 100, 512, 4, 64, FAKE, None) == ALIGN
+    assert f(FAKE, 100, 516, 4, 64, FAKE, None) == ALIGN           # 1032-byte pitch
+    assert f(FAKE, 100, 512, 4, 64, ctypes.c_void_p(0x10008), None) == ALIGN
+
+
+def test_attn_select_validation(L):
+    f = L.q8_attn_select
+    #         pq    pk   Hq Hkv NB   D   k  kmax idx  cnt
+    assert f(FAKE, FAKE, 6, 4, 10, 128, 4, 4, FAKE, FAKE, None) == SHAPE   # Hq % Hkv
+    assert f(FAKE, FAKE, 4, 2, 10, 128, 1, 4, FAKE, FAKE, None) == SHAPE   # k < 2
+    assert f(FAKE, FAKE, 4, 2, 10, 128, 5, 4, FAKE, FAKE, None) == SHAPE   # kmax < k
+    assert f(FAKE, FAKE, 4, 2, 4097, 128, 4, 4, FAKE, FAKE, None) == SHAPE
+    assert f(None, None, 4, 2, 0, 128, 4, 4, None, None, None) == OK
+    for i in range(4):
+        args = [FAKE, FAKE, 4, 2, 10, 128, 4, 4, FAKE, FAKE]
+        args[[0, 1, 8, 9][i]] = None
+        assert f(*args, None) == NULL
+    assert f(ODD, FAKE, 4, 2, 10, 128, 4, 4, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, FAKE, 4, 2, 10, 128, 4, 4, FAKE, ODD, None) == ALIGN
+
+
+def test_attn_fwd_validation(L):
+    f = L.q8_attn_fwd
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, L=100, ldq=512, ldk=256, ldv=256, Hq=4, Hkv=2, D=128,
+                 idx=FAKE, cnt=FAKE, kmax=4, dt=1, out=FAKE, ldo=512)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["L"], a["ldq"], a["ldk"], a["ldv"], a["Hq"], a["Hkv"],
+                 a["D"], a["idx"], a["cnt"], a["kmax"], a["dt"], a["out"], a["ldo"], None)
+    assert call(dt=3) == DTYPE
+    assert call(Hkv=3) == SHAPE
+    assert call(D=256, ldq=1024, ldk=512, ldv=512, ldo=1024) == SHAPE
+    assert call(ldq=500) == SHAPE and call(ldk=200) == SHAPE and call(ldo=256) == SHAPE
+    assert call(kmax=0) == SHAPE
+    assert call(L=64 * 4096 + 1) == SHAPE
+    assert call(ldq=1 << 24) == SHAPE
+    assert call(q=None, L=0) == OK
+    for name in ("q", "k", "v", "idx", "cnt", "out"):
+        assert call(**{name: None}) == NULL
+    assert call(q=ODD) == ALIGN and call(v=ctypes.c_void_p(0x10008)) == ALIGN
+    assert call(ldq=516) == ALIGN
+    assert call(dt=0, out=ctypes.c_void_p(0x10008)) == ALIGN        # fp32 out needs 16
+    assert call(dt=1, out=ctypes.c_void_p(0x10008)) not in (NULL, SHAPE, ALIGN, DTYPE)
+    assert call(dt=1, ldo=514) == ALIGN
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):

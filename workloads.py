@@ -31,6 +31,14 @@ bytes = 17.2 GB.  Each row is
   the outlier channels of attention keys) and per-row gains g_r = 2^U(-2, 2),
   rounded to bfloat16 where the workload is bfloat16.
 
+Attention inputs (block-sparse prefill attention, same pages, attention item
+of the engine's list; no shapes given): token-major bfloat16 Q [L][Hq*D] and
+K, V [L][Hkv*D] with block structure for the selection to find -- every
+(K/V head, 64-token block) has a topic vector c ~ N(0, 1); K rows are
+N(0, 1) + c of their block; every (query head, query block) picks 4 earlier
+blocks (uniformly, with repetition) and its Q rows are N(0, 1) + 0.75 times
+the sum of those blocks' topics; V rows are N(0, 1).
+
 Streams: numpy ``default_rng(SeedSequence([seed, case, tensor]))``; the
 device generator for full-size KV caches uses torch's Philox stream seeded
 with the same three numbers folded into one.
@@ -122,6 +130,50 @@ def kv_rows_device(R: int, D: int, case: int, device, tensor: int = 3, seed: int
         g = torch.exp2(torch.rand((r1 - r0, 1), generator=gen, device=device) * 4.0 - 2.0)
         out[r0:r1] = (z * c * g).to(torch.bfloat16)
     return out
+
+
+def attn_qkv(L: int, Hq: int, Hkv: int, D: int, case: int, seed: int = 0):
+    """(q, k, v) uint16 bfloat16 bits, token-major (see the module docstring)."""
+    r = rng(case, 5, seed)
+    NB = (L + 63) // 64
+    topic = r.standard_normal((Hkv, NB, D)).astype(np.float32)
+    blk = np.arange(L) // 64
+    k = r.standard_normal((L, Hkv, D)).astype(np.float32) + topic[:, blk, :].transpose(1, 0, 2)
+    picks = (r.random((Hq, NB, 4)) * np.maximum(np.arange(NB), 1)[None, :, None]).astype(np.int64)
+    g = np.arange(Hq) // (Hq // Hkv)
+    qt = 0.75 * topic[g[:, None, None], picks, :].sum(axis=2)          # [Hq][NB][D]
+    q = r.standard_normal((L, Hq, D)).astype(np.float32) + qt[:, blk, :].transpose(1, 0, 2)
+    v = r.standard_normal((L, Hkv, D)).astype(np.float32)
+    return (f32_to_bf16_bits(q.reshape(L, Hq * D)), f32_to_bf16_bits(k.reshape(L, Hkv * D)),
+            f32_to_bf16_bits(v.reshape(L, Hkv * D)))
+
+
+def attn_qkv_device(L: int, Hq: int, Hkv: int, D: int, case: int, device, seed: int = 0):
+    """The distribution of attn_qkv drawn on the device as bfloat16 tensors
+    (for sequences too long to draw on the host); a different stream."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed((seed * 1000003 + case) * 1000003 + 5)
+    NB = (L + 63) // 64
+    topic = torch.randn((Hkv, NB, D), generator=gen, device=device)
+    blk = torch.arange(L, device=device) // 64
+    k = torch.empty((L, Hkv * D), dtype=torch.bfloat16, device=device)
+    v = torch.empty((L, Hkv * D), dtype=torch.bfloat16, device=device)
+    q = torch.empty((L, Hq * D), dtype=torch.bfloat16, device=device)
+    picks = (torch.rand((Hq, NB, 4), generator=gen, device=device)
+             * torch.clamp(torch.arange(NB, device=device), min=1)[None, :, None]).long()
+    g = torch.arange(Hq, device=device) // (Hq // Hkv)
+    qt = 0.75 * topic[g[:, None, None], picks, :].sum(dim=2)          # [Hq][NB][D]
+    step = 8192
+    for t0 in range(0, L, step):
+        t1 = min(L, t0 + step)
+        b = blk[t0:t1]
+        kk = torch.randn((t1 - t0, Hkv, D), generator=gen, device=device) + topic[:, b, :].transpose(0, 1)
+        k[t0:t1] = kk.reshape(t1 - t0, -1).to(torch.bfloat16)
+        v[t0:t1] = torch.randn((t1 - t0, Hkv * D), generator=gen, device=device).to(torch.bfloat16)
+        qq = torch.randn((t1 - t0, Hq, D), generator=gen, device=device) + qt[:, b, :].transpose(0, 1)
+        q[t0:t1] = qq.reshape(t1 - t0, -1).to(torch.bfloat16)
+    return q, k, v
 
 
 @dataclass(frozen=True)
