@@ -6,7 +6,8 @@ One step = one pass of the whole path over one batch of synthetic input:
            the same step fused, q8_gemm_act (quantise inside the decode kernel)
   (after the timed steps, apart from them: the 3-bit KV-cache codec,
            q8_kv3_encode / q8_kv3_decode, on one layer's K and V at 256K
-           context, in "kv3")
+           context, in "kv3"; block-sparse attention prefill, q8_attn_*, at
+           64K tokens, in "attn")
   gated FFN step: q8_gemm_swiglu (gate+up product, silu(g)*u, Q8_0 for the
            down projection) at M2048 with I = 6144 hidden units (2I = 12288,
            the prefill weight's size), and at M=1 and M=4
@@ -279,6 +280,7 @@ def main():
               "traffic": measured_traffic("swiglu_prefill_traffic.json", "q8_gemm.hip", None)}
 
     kv3 = kv3_bench(q8, workloads, torch, np, dev)
+    attn = attn_bench(q8, workloads, torch, np, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -298,6 +300,7 @@ def main():
         "decode": dec,
         "swiglu": swiglu,
         "kv3": kv3,
+        "attn": attn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -346,6 +349,59 @@ def kv3_bench(q8, workloads, torch, np, dev, reps=20):
             "relative_mse_first_65536_rows": round(float(err), 5),
             "encode_traffic": measured_traffic("kv3_encode_traffic.json", "q8_kv3.hip", alg),
             "decode_traffic": measured_traffic("kv3_decode_traffic.json", "q8_kv3.hip", alg)}
+
+
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 matrix cores
+
+
+def attn_bench(q8, workloads, torch, np, dev, reps=10):
+    """Block-sparse causal attention prefill: 64K tokens, 32 query heads over
+    8 K/V heads, D = 128, 64 key blocks of 64 tokens per query block (block
+    0, the diagonal and 62 selected).  Pooling, selection and the forward
+    pass are timed with an event pair around each launch; the forward pass's
+    algorithmic work is 4 D flops per attended (query, key) pair (two
+    products), counted from the lists."""
+    L, Hq, Hkv, D, k = 65536, 32, 8, 128, 64
+    q, kk, v = workloads.attn_qkv_device(L, Hq, Hkv, D, 700, dev)
+    NB = (L + 63) // 64
+    pq = torch.empty((Hq, NB, D), dtype=torch.float32, device=dev)
+    pk = torch.empty((Hkv, NB, D), dtype=torch.float32, device=dev)
+    idx = torch.empty((Hq, NB, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((Hq, NB), dtype=torch.int32, device=dev)
+    out = torch.empty((L, Hq * D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(call):
+        for _ in range(2):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3   # us
+
+    pool_us = timed(lambda: (q8.q8_attn_pool(q, Hq, D, out=pq), q8.q8_attn_pool(kk, Hkv, D, out=pk)))
+    sel_us = timed(lambda: q8.q8_attn_select(pq, pk, k, idx=idx, cnt=cnt))
+    fwd_us = timed(lambda: q8.q8_attn_fwd(q, kk, v, Hq, Hkv, D, idx, cnt, out=out))
+    c = cnt.cpu().numpy().astype(np.int64)            # [Hq][NB]
+    rows = np.full(NB, 64, dtype=np.int64)
+    rows[-1] = L - 64 * (NB - 1)                       # queries of the last block
+    # every listed block below the diagonal: rows x 64 keys; the diagonal:
+    # the causal triangle
+    pairs = int(((c - 1) * rows[None, :] * 64 + (rows * (rows + 1) // 2)[None, :]).sum())
+    flops = 4.0 * D * pairs
+    tflops = flops / (fwd_us * 1e-6) / 1e12
+    return {"workload": "prefill L %d, %d query heads over %d K/V heads, D %d, %d blocks of 64 "
+                        "per query block, bf16" % (L, Hq, Hkv, D, k),
+            "fwd_us": round(fwd_us, 1), "fwd_tflops": round(tflops, 1),
+            "fwd_frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flops": flops, "attended_pairs": int(pairs),
+            "density": round(pairs / (Hq * L * (L + 1) / 2), 4),
+            "pool_us": round(pool_us, 1), "select_us": round(sel_us, 1),
+            "total_us": round(pool_us + sel_us + fwd_us, 1)}
 
 
 def cpu_baseline(seconds, qa_t, da_t, packs, N, K):

@@ -27,7 +27,10 @@
 //     L); LDS rows are padded so that the 16 lanes of each operand read hit
 //     distinct banks.
 // The softmax runs in base 2: scores are scaled by log2(e)/sqrt(D) and
-// exponentiated with exp2.
+// exponentiated with exp2 (v_exp_f32; a result below 2^-126 of the row's
+// maximum term flushes to zero, which no output can resolve).  The running
+// maximum is raised lazily (by steps of more than 2^8), so the output is
+// rescaled only when a block brings a clearly larger score.
 #include <float.h>
 
 #include "q8_kernels.h"
@@ -176,7 +179,7 @@ struct FwdLds {
 };
 
 template <int D, bool kBf16Out>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(
+__global__ __launch_bounds__(256, 3) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int64_t L, int64_t ldq, int64_t ldk, int64_t ldv, int64_t Hq, int64_t Hkv, int64_t NB,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int kmax,
@@ -221,49 +224,70 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
   const int n = n_raw < 0 ? 0 : (n_raw > kmax ? kmax : n_raw);
   const int32_t* list = idx + (h * NB + i) * kmax;
   const int tid = threadIdx.x;
-  for (int bi = 0; bi < n; ++bi) {
-    const int64_t j = list[bi];
-    if (j < 0 || j > i) continue;                // uniform: every lane reads the same entry
+  auto next_valid = [&](int b) {                 // uniform
+    for (; b < n; ++b) {
+      const int32_t j = list[b];
+      if (j >= 0 && j <= i) break;
+    }
+    return b;
+  };
+
+  // Global loads of a K/V block into registers, issued one block ahead.
+  // K: 16-byte chunks, row e / (D/8), column chunk e % (D/8).  V: a thread
+  // takes 4 consecutive keys (quad kq = e % 16) x 8 columns (octet
+  // dc = e / 16), so that its transposed 8-byte writes to LDS fall on
+  // distinct banks across 32 lanes.
+  constexpr int kKPer = kBlk * D / 8 / 256;      // K chunks per thread
+  constexpr int kVGroups = (kBlk / 4) * (D / 8); // (key quad, column octet) pairs
+  static_assert(kVGroups <= 256, "one V group per thread");
+  v4u kreg[kKPer], vreg[4];
+  auto load_block = [&](int64_t j) {
     const int64_t rows = L - j * kBlk < kBlk ? L - j * kBlk : kBlk;
-    __syncthreads();                             // the previous block's LDS reads are done
-    {
-      // K block: 64 rows x D -> lds.k[row][d]; 16-byte chunks, D/8 per row
-      const __amdgpu_buffer_rsrc_t rk = rows_rsrc(K + j * kBlk * ldk + g * D, static_cast<uint32_t>(rows * ldk * 2));
-      constexpr int kChunks = kBlk * D / 8;
-      static_assert(kChunks % 256 == 0, "K chunks per thread");
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(K + j * kBlk * ldk + g * D, static_cast<uint32_t>(rows * ldk * 2));
 #pragma unroll
-      for (int e0 = 0; e0 < kChunks; e0 += 256) {
-        const int e = e0 + tid, row = e / (D / 8), cc = e % (D / 8);
-        const v4u w = __builtin_amdgcn_raw_buffer_load_b128(
-            rk, static_cast<uint32_t>((row * ldk + 8 * cc) * 2), 0, 0);
-        *reinterpret_cast<v4u*>(&lds.k[row * Lds::kKPitch + 8 * cc]) = w;
-      }
-      // V block transposed: a thread takes 4 consecutive keys x 8 columns
-      // and writes, per column, the 4 keys as one 8-byte word of V^T
+    for (int u = 0; u < kKPer; ++u) {
+      const int e = u * 256 + tid, row = e / (D / 8), cc = e % (D / 8);
+      kreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, static_cast<uint32_t>((row * ldk + 8 * cc) * 2), 0, 0);
+    }
+    if (tid < kVGroups) {
       const __amdgpu_buffer_rsrc_t rv = rows_rsrc(V + j * kBlk * ldv + g * D, static_cast<uint32_t>(rows * ldv * 2));
-      constexpr int kGroups = (kBlk / 4) * (D / 8);   // (key quad, column octet) pairs
+      const int kq = tid % 16, dc = tid / 16;
 #pragma unroll
-      for (int e0 = 0; e0 < kGroups; e0 += 256) {
-        const int e = e0 + tid, dc = e % (D / 8), kq = e / (D / 8);
-        if (kGroups % 256 != 0 && e >= kGroups) break;   // D = 64: 128 groups
-        v4u r4[4];
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(
+            rv, static_cast<uint32_t>(((4 * kq + r) * ldv + 8 * dc) * 2), 0, 0);
+    }
+  };
+  auto store_block = [&]() {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          r4[r] = __builtin_amdgcn_raw_buffer_load_b128(
-              rv, static_cast<uint32_t>(((4 * kq + r) * ldv + 8 * dc) * 2), 0, 0);
+    for (int u = 0; u < kKPer; ++u) {
+      const int e = u * 256 + tid, row = e / (D / 8), cc = e % (D / 8);
+      *reinterpret_cast<v4u*>(&lds.k[row * Lds::kKPitch + 8 * cc]) = kreg[u];
+    }
+    if (tid < kVGroups) {
+      const int kq = tid % 16, dc = tid / 16;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // columns 8dc + 2w (low halves) and 8dc + 2w + 1 (high halves)
-          const uint32_t lo01 = __builtin_amdgcn_perm(r4[1][w], r4[0][w], 0x05040100u);
-          const uint32_t lo23 = __builtin_amdgcn_perm(r4[3][w], r4[2][w], 0x05040100u);
-          const uint32_t hi01 = __builtin_amdgcn_perm(r4[1][w], r4[0][w], 0x07060302u);
-          const uint32_t hi23 = __builtin_amdgcn_perm(r4[3][w], r4[2][w], 0x07060302u);
-          *reinterpret_cast<v2u*>(&lds.vt[(8 * dc + 2 * w) * Lds::kVPitch + 4 * kq]) = v2u{lo01, lo23};
-          *reinterpret_cast<v2u*>(&lds.vt[(8 * dc + 2 * w + 1) * Lds::kVPitch + 4 * kq]) = v2u{hi01, hi23};
-        }
+      for (int w = 0; w < 4; ++w) {
+        // columns 8dc + 2w (low halves) and 8dc + 2w + 1 (high halves)
+        const uint32_t lo01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
+        *reinterpret_cast<v2u*>(&lds.vt[(8 * dc + 2 * w) * Lds::kVPitch + 4 * kq]) = v2u{lo01, lo23};
+        *reinterpret_cast<v2u*>(&lds.vt[(8 * dc + 2 * w + 1) * Lds::kVPitch + 4 * kq]) = v2u{hi01, hi23};
       }
     }
+  };
+
+  int bi = next_valid(0);
+  if (bi < n) load_block(list[bi]);
+  while (bi < n) {
+    const int64_t j = list[bi];
+    __syncthreads();                             // the previous block's LDS reads are done
+    store_block();
     __syncthreads();
+    bi = next_valid(bi + 1);
+    if (bi < n) load_block(list[bi]);            // in flight during this block's products
 
     // scores: s[kt][r] = S[key 16 kt + 4 gq + r][query c], scaled to base 2
     f4 s[4];
@@ -277,36 +301,44 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
       }
       s[kt] = acc;
     }
+    // causal mask, in the diagonal block only (uniform branch)
+    if (j == i) {
+      const int qi = static_cast<int>(q - i * kBlk);   // query's row in the block
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * kt + 4 * gq + r > qi) s[kt][r] = -INFINITY;
+    }
+    // row maximum over the block's keys (4 lanes share a query), in base 2
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = s[kt][r] * scale_log2;
-        const int64_t key = j * kBlk + 16 * kt + 4 * gq + r;
-        if (key > q) v = -INFINITY;               // causal (only in the diagonal block)
-        s[kt][r] = v;
-        mx = fmaxf(mx, v);
-      }
+      mx = fmaxf(fmaxf(mx, fmaxf(s[kt][0], s[kt][1])), fmaxf(s[kt][2], s[kt][3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = exp2f(m - m_new);
-    float rs = 0.0f;
+    mx *= scale_log2;
+    // Lazy rescaling: the reference maximum m only moves when a block's
+    // maximum exceeds it by more than 8, so exponentials stay <= 2^8 (exact
+    // ratios; bfloat16 holds them) and the output is rarely rescaled.
+    const bool raise = mx > m + 8.0f;
+    if (__any(raise)) {
+      const float m_new = raise ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      m = m_new;
+    }
+    // p = 2^(s * log2(e)/sqrt(D) - m); this lane's part of the row sum
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(s[kt][r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], scale_log2, -m));
         s[kt][r] = p;
-        rs += p;
+        lsum += p;
       }
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
-    lsum = lsum * alpha + rs;
-    m = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
 
     // O^T += V^T P^T, two 32-key chunks: slots 8 gq .. 8 gq + 3 are keys
     // 32 pc + 4 gq + r (tile 2 pc), slots 8 gq + 4 .. + 7 keys 32 pc + 16 + 4 gq + r
@@ -332,6 +364,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
     }
   }
 
+  // the 4 lanes of a query hold parts of its row sum
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
   // O[q][h*D + 16 dt + 4 gq + r] = o[dt][r] / lsum
   if (q < L) {
     const float inv = 1.0f / lsum;
