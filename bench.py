@@ -357,7 +357,7 @@ PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 matrix cores
 def attn_bench(q8, workloads, torch, np, dev, reps=10):
     """Block-sparse causal attention prefill: 64K tokens, 32 query heads over
     8 K/V heads, D = 128, 64 key blocks of 64 tokens per query block (block
-    0, the diagonal and 62 selected).  Pooling, selection and the forward
+    0, the diagonal and 62 selected; one list per K/V head).  Pooling, selection and the forward
     pass are timed with an event pair around each launch; the forward pass's
     algorithmic work is 4 D flops per attended (query, key) pair (two
     products), counted from the lists."""
@@ -366,8 +366,8 @@ def attn_bench(q8, workloads, torch, np, dev, reps=10):
     NB = (L + 63) // 64
     pq = torch.empty((Hq, NB, D), dtype=torch.float32, device=dev)
     pk = torch.empty((Hkv, NB, D), dtype=torch.float32, device=dev)
-    idx = torch.empty((Hq, NB, k), dtype=torch.int32, device=dev)
-    cnt = torch.empty((Hq, NB), dtype=torch.int32, device=dev)
+    idx = torch.empty((Hkv, NB, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((Hkv, NB), dtype=torch.int32, device=dev)
     out = torch.empty((L, Hq * D), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -386,7 +386,7 @@ def attn_bench(q8, workloads, torch, np, dev, reps=10):
     pool_us = timed(lambda: (q8.q8_attn_pool(q, Hq, D, out=pq), q8.q8_attn_pool(kk, Hkv, D, out=pk)))
     sel_us = timed(lambda: q8.q8_attn_select(pq, pk, k, idx=idx, cnt=cnt))
     fwd_us = timed(lambda: q8.q8_attn_fwd(q, kk, v, Hq, Hkv, D, idx, cnt, out=out))
-    c = cnt.cpu().numpy().astype(np.int64)            # [Hq][NB]
+    c = np.repeat(cnt.cpu().numpy().astype(np.int64), Hq // Hkv, axis=0)   # per query head
     rows = np.full(NB, 64, dtype=np.int64)
     rows[-1] = L - 64 * (NB - 1)                       # queries of the last block
     # every listed block below the diagonal: rows x 64 keys; the diagonal:

@@ -298,19 +298,23 @@ q8_status q8_kv3_decode(const uint8_t *codes, const float *scales, int64_t R, in
  *   H * NB * D floats, NB = ceil(L/64), and is 16-byte aligned.
  *   x: 16-byte aligned, ldx >= H*D, ldx*2 % 16 == 0, ldx < 2^24.
  *
- * q8_attn_select: for every query head h and query block i, the key blocks
- *   it attends to: block 0, block i, and the k - 2 blocks 0 < j < i with the
- *   highest score pooled_q[h][i] . pooled_k[g][j] (higher score first, the
- *   lower j on equal scores); every block j <= i when k >= i + 1.
- *   idx [Hq][NB][kmax] int32 receives them in ascending order, -1 after the
- *   last; cnt [Hq][NB] int32 receives min(k, i + 1).  2 <= k <= kmax,
+ * q8_attn_select: for every K/V head g and query block i, the key blocks
+ *   the block's queries attend to, shared by the Hq/Hkv query heads of g's
+ *   group (they read the same K and V): block 0, block i, and the k - 2
+ *   blocks 0 < j < i with the highest score
+ *   (sum over the group's heads h of pooled_q[h][i]) . pooled_k[g][j]
+ *   (higher score first, the lower j on equal scores); every block j <= i
+ *   when k >= i + 1.  idx [Hkv][NB][kmax] int32 receives them in ascending
+ *   order, -1 after the last; cnt [Hkv][NB] int32 receives min(k, i + 1).
+ *   2 <= k <= kmax,
  *   NB <= 4096.  Scores are binary32 dot products of the binary32 pooled
  *   rows; blocks whose scores differ from the k-2'th by a few binary32
  *   units may be chosen either way.
  *
  * q8_attn_fwd: out[t][h*D + d] = sum_u p_u V[u][g*D + d] / sum_u p_u over
- *   the keys u <= t of the blocks listed for t's block (idx/cnt as written by
- *   q8_attn_select, or any list of blocks 0 <= j <= i in ascending order),
+ *   the keys u <= t of the blocks listed for (g, t's block) (idx/cnt
+ *   [Hkv][NB] as written by q8_attn_select, or any lists of blocks
+ *   0 <= j <= i in ascending order),
  *   p_u = exp(q_t . k_u / sqrt(D) - max).  Scores and sums in binary32 on
  *   the bf16 matrix cores, p rounded to bfloat16 for the product with V (as
  *   in FlashAttention), so |out - exact| <= ~2^-8 * sum_u p_u |V_u| / sum_u p_u

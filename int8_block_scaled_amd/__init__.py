@@ -337,8 +337,8 @@ def q8_attn_pool(x: torch.Tensor, H: int, D: int, out: torch.Tensor = None) -> t
 
 def q8_attn_select(pooled_q: torch.Tensor, pooled_k: torch.Tensor, k: int, kmax: int = None,
                    idx: torch.Tensor = None, cnt: torch.Tensor = None):
-    """Pooled rows [Hq][NB][D], [Hkv][NB][D] -> (idx int32 [Hq][NB][kmax],
-    cnt int32 [Hq][NB]): the key blocks of every query block."""
+    """Pooled rows [Hq][NB][D], [Hkv][NB][D] -> (idx int32 [Hkv][NB][kmax],
+    cnt int32 [Hkv][NB]): the key blocks of every query block, per K/V head."""
     for name, t in (("pooled_q", pooled_q), ("pooled_k", pooled_k)):
         _need_cuda(name, t)
         if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 3:
@@ -347,9 +347,9 @@ def q8_attn_select(pooled_q: torch.Tensor, pooled_k: torch.Tensor, k: int, kmax:
     Hkv = pooled_k.shape[0]
     kmax = k if kmax is None else kmax
     if idx is None:
-        idx = torch.empty((Hq, NB, kmax), dtype=torch.int32, device=pooled_q.device)
+        idx = torch.empty((Hkv, NB, kmax), dtype=torch.int32, device=pooled_q.device)
     if cnt is None:
-        cnt = torch.empty((Hq, NB), dtype=torch.int32, device=pooled_q.device)
+        cnt = torch.empty((Hkv, NB), dtype=torch.int32, device=pooled_q.device)
     _check("q8_attn_select", _load().q8_attn_select(_ptr(pooled_q), _ptr(pooled_k), Hq, Hkv, NB, D,
                                                     k, kmax, _ptr(idx), _ptr(cnt),
                                                     _stream(pooled_q)))
@@ -359,14 +359,18 @@ def q8_attn_select(pooled_q: torch.Tensor, pooled_k: torch.Tensor, k: int, kmax:
 def q8_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, Hq: int, Hkv: int, D: int,
                 idx: torch.Tensor, cnt: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
                 out: torch.Tensor = None) -> torch.Tensor:
-    """Block-sparse causal attention over the listed key blocks: q [L][>=Hq*D],
-    k, v [L][>=Hkv*D] bfloat16 -> out [L][Hq*D] (bfloat16 or float32)."""
+    """Block-sparse causal attention over the listed key blocks (idx
+    [Hkv][NB][kmax], cnt [Hkv][NB]): q [L][>=Hq*D], k, v [L][>=Hkv*D]
+    bfloat16 -> out [L][Hq*D] (bfloat16 or float32)."""
     ldq, ldk, ldv = _bf16_rows("q", q), _bf16_rows("k", k), _bf16_rows("v", v)
     for name, t in (("idx", idx), ("cnt", cnt)):
         _need_cuda(name, t)
         if t.dtype != torch.int32 or not t.is_contiguous():
             raise TypeError("%s must be contiguous int32" % name)
     L = q.shape[0]
+    NB = (L + 63) // 64
+    if idx.dim() != 3 or tuple(idx.shape[:2]) != (Hkv, NB) or tuple(cnt.shape) != (Hkv, NB):
+        raise TypeError("idx must be [Hkv][NB][kmax] and cnt [Hkv][NB], NB = ceil(L/64)")
     if out is None:
         out = torch.empty((L, Hq * D), dtype=out_dtype, device=q.device)
     odt = _act_dtype(out)

@@ -259,7 +259,7 @@ q8_status q8_attn_select(const float* pooled_q, const float* pooled_k, int64_t H
                          int64_t NB, int64_t D, int k, int kmax, int32_t* idx, int32_t* cnt,
                          void* stream) {
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || NB < 0 || NB > kMaxAttnBlocks || !valid_attn_dim(D) ||
-      k < 2 || kmax < k || Hq * NB >= kMaxDim)
+      k < 2 || kmax < k || Hkv * NB >= kMaxDim)
     return Q8_ERR_SHAPE;
   if (NB == 0) return Q8_OK;
   if (pooled_q == nullptr || pooled_k == nullptr || idx == nullptr || cnt == nullptr)

@@ -7,7 +7,8 @@
 // give no more; the operation is specified in include/q8.h (q8_attn_pool,
 // q8_attn_select, q8_attn_fwd): 64-token blocks, each query block attending
 // to block 0, its own (diagonal, causally masked) block and the top-scoring
-// earlier blocks by the dot product of block-mean-pooled Q and K.
+// earlier blocks by the dot product of block-mean-pooled Q and K; one list
+// per K/V head, shared by its group of query heads.
 //
 // The forward kernel is a FlashAttention forward pass over the listed key
 // blocks, on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16):
@@ -86,10 +87,10 @@ __global__ __launch_bounds__(256) void attn_pool_kernel(const uint16_t* __restri
 constexpr int kSelThreads = 256;
 constexpr int kMaxBlocks = 4096;               // 256K tokens
 
-// One workgroup per (query head, query block i): scores of blocks 0 < j < i
-// against the pooled query row, a bitonic sort by (score descending, block
-// ascending), then block 0, block i and the first (k - 2) of the sort,
-// written in ascending order.
+// One workgroup per (K/V head g, query block i): scores of blocks 0 < j < i,
+// the sum of the group's pooled query rows against the pooled key rows, a
+// bitonic sort by (score descending, block ascending), then block 0, block
+// i and the first (k - 2) of the sort, written in ascending order.
 template <int D>
 __global__ __launch_bounds__(kSelThreads) void attn_select_kernel(
     const float* __restrict__ pq, const float* __restrict__ pk, int64_t Hq, int64_t Hkv,
@@ -98,15 +99,19 @@ __global__ __launch_bounds__(kSelThreads) void attn_select_kernel(
   __shared__ int32_t id[kMaxBlocks];
   __shared__ uint8_t take[kMaxBlocks];
   __shared__ float qrow[D];
-  const int64_t h = blockIdx.x / NB, i = blockIdx.x % NB;
-  const int64_t g = h / (Hq / Hkv);
+  const int64_t g = blockIdx.x / NB, i = blockIdx.x % NB;
+  const int64_t G = Hq / Hkv;
   const int tid = threadIdx.x;
-  int32_t* out = idx + (h * NB + i) * kmax;
+  int32_t* out = idx + (g * NB + i) * kmax;
   for (int m = tid; m < kmax; m += kSelThreads) out[m] = -1;
   for (int64_t j = tid; j <= i; j += kSelThreads) take[j] = (k >= i + 1 || j == 0 || j == i) ? 1 : 0;
-  if (tid == 0) cnt[h * NB + i] = static_cast<int32_t>(k >= i + 1 ? i + 1 : k);
+  if (tid == 0) cnt[g * NB + i] = static_cast<int32_t>(k >= i + 1 ? i + 1 : k);
   if (k < i + 1 && k > 2) {
-    for (int d = tid; d < D; d += kSelThreads) qrow[d] = pq[(h * NB + i) * D + d];
+    for (int d = tid; d < D; d += kSelThreads) {   // the group's query row
+      float a = 0.0f;
+      for (int64_t hh = 0; hh < G; ++hh) a += pq[((g * G + hh) * NB + i) * D + d];
+      qrow[d] = a;
+    }
     __syncthreads();
     // candidates 1 .. i-1, padded to a power of two with -inf
     const int ncand = static_cast<int>(i - 1);
@@ -188,10 +193,22 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(
   __shared__ Lds lds;
   constexpr int KC = D / 32;                     // 32-wide d chunks of a score product
   constexpr int DT = D / 16;                     // 16-row d tiles of the output
-  // later query blocks first (they have the most key blocks)
-  const int64_t wg = blockIdx.x;
-  const int64_t i = NB - 1 - wg / Hq, h = wg % Hq;
-  const int64_t g = h / (Hq / Hkv);
+  // Tiles (query block i, K/V head g), later blocks first (they list the
+  // most key blocks); the G = Hq/Hkv query heads of a tile share its list,
+  // so their workgroups are given ids 8 apart: workgroups are dealt to the
+  // 8 XCDs in turn, so the G of them run together on one XCD and read the
+  // listed K/V blocks through its L2.
+  const int64_t wg = blockIdx.x, G = Hq / Hkv, tiles = NB * Hkv;
+  int64_t t, hh;
+  if (tiles % 8 == 0) {
+    const int64_t x = wg % 8, y = wg / 8;
+    hh = y % G;
+    t = (y / G) * 8 + x;
+  } else {
+    t = wg / G;
+    hh = wg % G;
+  }
+  const int64_t i = NB - 1 - t / Hkv, g = t % Hkv, h = g * G + hh;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
   const int64_t q0 = i * kBlk + 16 * wave;       // the wave's first query
@@ -220,9 +237,9 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(
   // the list is device data: clamp its length and skip entries outside the
   // blocks a query block may see, so that no entry can move a load off its
   // buffer
-  const int n_raw = cnt[h * NB + i];
+  const int n_raw = cnt[g * NB + i];
   const int n = n_raw < 0 ? 0 : (n_raw > kmax ? kmax : n_raw);
-  const int32_t* list = idx + (h * NB + i) * kmax;
+  const int32_t* list = idx + (g * NB + i) * kmax;   // the K/V head's list
   const int tid = threadIdx.x;
   auto next_valid = [&](int b) {                 // uniform
     for (; b < n; ++b) {
@@ -407,7 +424,7 @@ hipError_t launch_attn_pool(const uint16_t* x, int64_t L, int64_t ldx, int64_t H
 hipError_t launch_attn_select(const float* pq, const float* pk, int64_t Hq, int64_t Hkv, int64_t NB,
                               int64_t D, int k, int kmax, int32_t* idx, int32_t* cnt,
                               hipStream_t stream) {
-  const uint32_t grid = static_cast<uint32_t>(Hq * NB);
+  const uint32_t grid = static_cast<uint32_t>(Hkv * NB);
   if (D == 128)
     hipLaunchKernelGGL((attn_select_kernel<128>), dim3(grid), dim3(kSelThreads), 0, stream, pq, pk,
                        Hq, Hkv, NB, k, kmax, idx, cnt);

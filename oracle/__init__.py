@@ -278,14 +278,15 @@ class Oracle:
 
     def attn_select(self, pq, pk, k, kmax=None):
         """Pooled rows ([Hq][NB][D], [Hkv][NB][D]) -> (idx int32
-        [Hq][NB][kmax], cnt int32 [Hq][NB]): block 0, the diagonal block and
-        the top-scoring others, ascending, -1 past cnt."""
+        [Hkv][NB][kmax], cnt int32 [Hkv][NB]): per K/V head, block 0, the
+        diagonal block and the others scoring highest against the sum of the
+        group's pooled query rows, ascending, -1 past cnt."""
         pq, pk = _c(pq, np.float64), _c(pk, np.float64)
         Hq, NB, D = pq.shape
         Hkv = pk.shape[0]
         kmax = k if kmax is None else kmax
-        idx = np.empty((Hq, NB, kmax), dtype=np.int32)
-        cnt = np.empty((Hq, NB), dtype=np.int32)
+        idx = np.empty((Hkv, NB, kmax), dtype=np.int32)
+        cnt = np.empty((Hkv, NB), dtype=np.int32)
         self.L.q8ref_attn_select(_p(pq), _p(pk), Hq, Hkv, NB, D, k, kmax, _p(idx), _p(cnt))
         return idx, cnt
 

@@ -478,10 +478,11 @@ void q8ref_kv3_decode(const uint8_t *codes, const float *scales, int64_t R, int 
 /*   Blocks of 64 tokens; block i holds tokens 64i .. min(64i+63, L-1).     */
 /*   Pooled rows: the mean over a block's tokens of Q (per query head) and  */
 /*   of K (per K/V head).                                                   */
-/*   Selection: query block i of head h keeps block 0, block i, and the     */
-/*   top (k - 2) blocks 0 < j < i by score q_i . k_j of the pooled rows     */
-/*   (ties: lower j first); all blocks j <= i when k >= i + 1.  Listed in   */
-/*   ascending order, cnt = min(k, i + 1).                                  */
+/*   Selection, per K/V head g (shared by its group of Hq/Hkv query heads): */
+/*   query block i keeps block 0, block i, and the top (k - 2) blocks      */
+/*   0 < j < i by score (sum over the group's heads of their pooled query   */
+/*   rows) . (pooled key row of block j) (ties: lower j first); all blocks  */
+/*   j <= i when k >= i + 1.  Listed in ascending order, cnt = min(k,i+1). */
 /*   Output: token t of query block i attends to the keys u <= t of its     */
 /*   listed blocks: o = sum_u p_u v_u / sum_u p_u, p_u = exp(q.k_u / sqrt D */
 /*   - max), computed in double.                                            */
@@ -509,13 +510,13 @@ void q8ref_attn_pool(const uint16_t *x, int64_t L, int64_t ldx, int64_t H, int D
         }
 }
 
-/* idx [Hq][NB][kmax] (ascending, the rest -1), cnt [Hq][NB]; k <= kmax. */
+/* idx [Hkv][NB][kmax] (ascending, the rest -1), cnt [Hkv][NB]; k <= kmax. */
 void q8ref_attn_select(const double *pq, const double *pk, int64_t Hq, int64_t Hkv, int64_t NB,
                        int D, int k, int kmax, int32_t *idx, int32_t *cnt)
 {
     const int64_t group = Hq / Hkv;
     #pragma omp parallel for collapse(2) schedule(dynamic, 16)
-    for (int64_t h = 0; h < Hq; ++h)
+    for (int64_t h = 0; h < Hkv; ++h)
         for (int64_t i = 0; i < NB; ++i) {
             int32_t *row = idx + (h * NB + i) * kmax;
             for (int m = 0; m < kmax; ++m) row[m] = -1;
@@ -528,13 +529,15 @@ void q8ref_attn_select(const double *pq, const double *pk, int64_t Hq, int64_t H
                 take[0] = 1;
                 take[i] = 1;
                 n = i > 0 ? 2 : 1;
-                const double *q = pq + (h * NB + i) * D;
+                double *q = calloc((size_t)D, sizeof(double));   /* the group's query row */
+                for (int64_t hq = h * group; hq < (h + 1) * group; ++hq)
+                    for (int d = 0; d < D; ++d) q[d] += pq[(hq * NB + i) * D + d];
                 while (n < k) {                          /* next best: highest score, lowest j */
                     int64_t best = -1;
                     double bs = 0.0;
                     for (int64_t j = 1; j < i; ++j) {
                         if (take[j]) continue;
-                        const double *kk = pk + ((h / group) * NB + j) * D;
+                        const double *kk = pk + (h * NB + j) * D;
                         double sc = 0.0;
                         for (int d = 0; d < D; ++d) sc += q[d] * kk[d];
                         if (best < 0 || sc > bs) { best = j; bs = sc; }
@@ -542,6 +545,7 @@ void q8ref_attn_select(const double *pq, const double *pk, int64_t Hq, int64_t H
                     take[best] = 1;
                     ++n;
                 }
+                free(q);
             }
             int m = 0;
             for (int64_t j = 0; j <= i; ++j)
@@ -560,8 +564,8 @@ static void attn_row(const uint16_t *Q, const uint16_t *K, const uint16_t *V, in
     const int64_t NB = (L + ATTN_BLK - 1) / ATTN_BLK, group = Hq / Hkv;
     const double scale = 1.0 / sqrt((double)D);
     const int64_t i = t / ATTN_BLK, g = h / group;
-    const int32_t *row = idx + (h * NB + i) * kmax;
-    const int n = cnt[h * NB + i];
+    const int32_t *row = idx + (g * NB + i) * kmax;       /* the K/V head's list */
+    const int n = cnt[g * NB + i];
     double *s = malloc(sizeof(double) * (size_t)n * ATTN_BLK);
     int64_t *u_of = malloc(sizeof(int64_t) * (size_t)n * ATTN_BLK);
     int ns = 0;

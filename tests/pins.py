@@ -589,12 +589,14 @@ def _sdpa(q, k, v, Hq, Hkv, D, allowed):
     return o[0].numpy().transpose(1, 0, 2).reshape(L, Hq * D)
 
 
-def _allowed_from_lists(idx, cnt, L):
-    Hq, NB, _ = idx.shape
+def _allowed_from_lists(idx, cnt, L, Hq):
+    """Lists per K/V head [Hkv][NB][kmax] -> mask per query head."""
+    Hkv, NB, _ = idx.shape
     allowed = np.zeros((Hq, L, L), dtype=bool)
     for h in range(Hq):
+        g = h // (Hq // Hkv)
         for i in range(NB):
-            for j in idx[h, i, :cnt[h, i]]:
+            for j in idx[g, i, :cnt[g, i]]:
                 allowed[h, 64 * i:64 * i + 64, 64 * j:64 * j + 64] = True
     return allowed & np.tril(np.ones((L, L), dtype=bool))[None]
 
@@ -621,16 +623,16 @@ def pin_attn_masked(orc):
     NB = (L + 63) // 64
     r = np.random.default_rng(8)
     kmax = 4
-    idx = np.full((Hq, NB, kmax), -1, np.int32)
-    cnt = np.zeros((Hq, NB), np.int32)
-    for h in range(Hq):
+    idx = np.full((Hkv, NB, kmax), -1, np.int32)
+    cnt = np.zeros((Hkv, NB), np.int32)
+    for g in range(Hkv):
         for i in range(NB):
             extra = [j for j in range(1, i) if r.random() < 0.4][:kmax - 2]
             blocks = sorted(set([0, i] + extra))
-            idx[h, i, :len(blocks)] = blocks
-            cnt[h, i] = len(blocks)
+            idx[g, i, :len(blocks)] = blocks
+            cnt[g, i] = len(blocks)
     out, _ = orc.attn_fwd(q, k, v, Hq, Hkv, D, idx, cnt)
-    ref = _sdpa(q, k, v, Hq, Hkv, D, _allowed_from_lists(idx, cnt, L))
+    ref = _sdpa(q, k, v, Hq, Hkv, D, _allowed_from_lists(idx, cnt, L, Hq))
     assert np.max(np.abs(out - ref)) < 1e-12, np.max(np.abs(out - ref))
 
 
@@ -691,6 +693,24 @@ def pin_attn_select(orc):
     # hand check of one row: i = 9, k = 4: scores 3 (j=1), 3 (3), 3 (6): keep 1, 3
     idx, cnt = orc.attn_select(pq, pk, 4)
     assert list(idx[0, 9, :4]) == [0, 1, 3, 9]
+    # a group of two query heads over one K/V head ranks by the sum of the
+    # heads' scores: head 0 rows e_0, head 1 rows e_1, K block j rows
+    # a_j e_0 + b_j e_1, so the score of block j is a_j + b_j.  Head 0 alone
+    # would keep blocks 1, 4 (a = 3, 2.5), head 1 alone 2, 3 (b = 3, 2); the
+    # sums are 3, 3, 4, 4.25, so the group keeps 3 and 4.
+    a = np.array([0, 3, 0, 2, 2.5, 0, 0, 0, 0, 0])
+    b = np.array([0, 0, 3, 2, 1.75, 0, 0, 0, 0, 0])
+    NB2 = a.size
+    q2 = np.zeros((64 * NB2, 2 * D), np.float32)
+    q2[:, 0] = 1.0
+    q2[:, D + 1] = 1.0
+    k2 = np.zeros((64 * NB2, D), np.float32)
+    for j in range(NB2):
+        k2[64 * j:64 * j + 64, 0] = a[j]
+        k2[64 * j:64 * j + 64, 1] = b[j]
+    idx2, cnt2 = orc.attn_select(orc.attn_pool(_bf16(q2), 2, D), orc.attn_pool(_bf16(k2), 1, D), 4)
+    assert idx2.shape == (1, NB2, 4)
+    assert list(idx2[0, 9, :4]) == [0, 3, 4, 9] and list(idx2[0, 5, :4]) == [0, 3, 4, 5]
 
 
 ALL_PINS = [pin_f16_roundtrip_all, pin_f16_vs_numpy, pin_quant_golden, pin_quant_exact_random,

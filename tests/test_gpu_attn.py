@@ -45,32 +45,36 @@ def _check_out(got, ref, mag, bf16_out, what):
 
 
 def _check_lists(idx_g, cnt_g, pq, pk, k, rows):
-    """GPU lists for the given (head, block) rows, against the selection rule
-    applied to the oracle's pooled rows (double): block 0 and the diagonal,
-    then every candidate scoring clearly above the cut ((k-2)'th best score)
-    and none clearly below it; within eps of the cut either choice is
-    right.  eps bounds the binary32 error of a GPU score."""
+    """GPU lists for the given (K/V head, block) rows, against the selection
+    rule applied to the oracle's pooled rows (double): block 0 and the
+    diagonal, then every candidate whose score (the group's summed pooled
+    query row against the pooled key row) lies clearly above the cut ((k-2)'th
+    best score) and none clearly below it; within eps of the cut either choice
+    is right.  eps bounds the binary32 error of a GPU score."""
     Hq, Hkv = pq.shape[0], pk.shape[0]
-    for h, i in rows:
-        g = h // (Hq // Hkv)
+    G = Hq // Hkv
+    assert idx_g.shape[0] == Hkv and cnt_g.shape == (Hkv, pq.shape[1])
+    for g, i in rows:
         n = min(k, i + 1)
-        assert int(cnt_g[h, i]) == n, (h, i, cnt_g[h, i], n)
-        a = [int(j) for j in idx_g[h, i, :n]]
-        assert a == sorted(set(a)) and 0 in a and i in a and max(a) <= i, (h, i, a)
-        assert np.all(idx_g[h, i, n:] == -1), (h, i)
+        assert int(cnt_g[g, i]) == n, (g, i, cnt_g[g, i], n)
+        a = [int(j) for j in idx_g[g, i, :n]]
+        assert a == sorted(set(a)) and 0 in a and i in a and max(a) <= i, (g, i, a)
+        assert np.all(idx_g[g, i, n:] == -1), (g, i)
         if k >= i + 1:
             assert a == list(range(i + 1))
             continue
+        q = pq[g * G:(g + 1) * G, i].sum(axis=0)
+        qa = np.abs(pq[g * G:(g + 1) * G, i]).sum(axis=0)
         cand = list(range(1, i))
-        sc = np.array([pq[h, i] @ pk[g, j] for j in cand])
-        eps = 5e-5 * np.array([np.abs(pq[h, i]) @ np.abs(pk[g, j]) for j in cand]) + 1e-6
+        sc = np.array([q @ pk[g, j] for j in cand])
+        eps = 5e-5 * np.array([qa @ np.abs(pk[g, j]) for j in cand]) + 1e-6
         cut = np.sort(sc)[::-1][k - 3] if k > 2 else np.inf
         chosen = set(a) - {0, i}
         for j, s_, e in zip(cand, sc, eps):
             if s_ > cut + e:
-                assert j in chosen, (h, i, j, s_, cut)
+                assert j in chosen, (g, i, j, s_, cut)
             elif s_ < cut - e:
-                assert j not in chosen, (h, i, j, s_, cut)
+                assert j not in chosen, (g, i, j, s_, cut)
 
 
 def _run(orc, L, Hq, Hkv, D, k, case, out_dtype=torch.bfloat16, pitch=0):
@@ -107,7 +111,7 @@ def test_attn_select(orc, L, Hq, Hkv, D, k):
     pkt = q8.q8_attn_pool(_dev_bf16(kb), Hkv, D)
     idx, cnt = q8.q8_attn_select(pqt, pkt, k, kmax=k + 2)
     NB = (L + 63) // 64
-    rows = [(h, i) for h in range(Hq) for i in range(NB)]
+    rows = [(g, i) for g in range(Hkv) for i in range(NB)]
     _check_lists(idx.cpu().numpy(), cnt.cpu().numpy(), pq, pk, k, rows)
     # the oracle's own lists satisfy the same rule (and equal the GPU's
     # wherever no score sits near the cut)
@@ -154,7 +158,7 @@ def test_attn_end_to_end(orc):
     out = q8.q8_attn_fwd(qt, kt, vt, Hq, Hkv, D, idx, cnt, out_dtype=torch.float32)
     idx_g, cnt_g = idx.cpu().numpy(), cnt.cpu().numpy()
     pq, pk = orc.attn_pool(qb, Hq, D), orc.attn_pool(kb, Hkv, D)
-    _check_lists(idx_g, cnt_g, pq, pk, k, [(h, i) for h in range(Hq) for i in range((L + 63) // 64)])
+    _check_lists(idx_g, cnt_g, pq, pk, k, [(g, i) for g in range(Hkv) for i in range((L + 63) // 64)])
     ref, mag = orc.attn_fwd(qb, kb, vb, Hq, Hkv, D, idx_g, cnt_g)
     _check_out(out.cpu().numpy(), ref, mag, False, "end to end")
 
@@ -162,15 +166,15 @@ def test_attn_end_to_end(orc):
 def test_attn_list_entries_outside_range_are_skipped(orc):
     """Entries outside [0, i] are skipped and cnt is clamped to kmax: the
     output equals attention over the remaining entries."""
-    L, Hq, Hkv, D = 400, 2, 1, 64
+    L, Hq, Hkv, D = 400, 4, 2, 64
     qb, kb, vb, qt, kt, vt = _run(orc, L, Hq, Hkv, D, 4, 93)
     NB = (L + 63) // 64
     kmax = 5
-    idx = np.full((Hq, NB, kmax), -1, np.int32)
-    cnt = np.zeros((Hq, NB), np.int32)
-    clean = np.full((Hq, NB, kmax), -1, np.int32)
-    ccnt = np.zeros((Hq, NB), np.int32)
-    for h in range(Hq):
+    idx = np.full((Hkv, NB, kmax), -1, np.int32)
+    cnt = np.zeros((Hkv, NB), np.int32)
+    clean = np.full((Hkv, NB, kmax), -1, np.int32)
+    ccnt = np.zeros((Hkv, NB), np.int32)
+    for h in range(Hkv):
         for i in range(NB):
             good = sorted(set([0, i] + ([i // 2] if i > 2 else [])))
             raw = [-3] + good + [i + 1 + h, NB + 7][: kmax - 1 - len(good)]
@@ -189,7 +193,7 @@ def test_attn_bench_workload_sampled(orc):
     D = 128, 64 blocks per query block), in the launches the benchmark
     times; 48 sampled (token, head) outputs (the first and last tokens
     included) against the oracle over the GPU's lists, and the lists of 16
-    sampled (head, block) rows checked against the oracle's scores."""
+    sampled (K/V head, block) rows checked against the oracle's scores."""
     L, Hq, Hkv, D, k = 65536, 32, 8, 128, 64
     qt, kt, vt = workloads.attn_qkv_device(L, Hq, Hkv, D, 700, DEV)
     say("attn bench workload L=%d" % L)
@@ -207,6 +211,6 @@ def test_attn_bench_workload_sampled(orc):
     got = np.stack([got[t, h * D:(h + 1) * D] for t, h in zip(tok, head)])
     _check_out(got, ref, mag, True, "bench layer")
     pq, pk = orc.attn_pool(qb, Hq, D), orc.attn_pool(kb, Hkv, D)
-    rows = list(zip(r.integers(0, Hq, 16).tolist(),
+    rows = list(zip(r.integers(0, Hkv, 16).tolist(),
                     [1023, 1022, 63, 64] + r.integers(0, 1024, 12).tolist()))
     _check_lists(idx_g, cnt_g, pq, pk, k, rows)

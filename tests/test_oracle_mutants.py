@@ -58,6 +58,8 @@ MUTANTS = {
     "attn_no_sink": ("                take[0] = 1;\n", "                take[1 < i ? 1 : 0] = 1;\n"),
     "attn_ties_high": ("if (best < 0 || sc > bs) { best = j; bs = sc; }",
                        "if (best < 0 || sc >= bs) { best = j; bs = sc; }"),
+    "attn_select_one_head": ("for (int64_t hq = h * group; hq < (h + 1) * group; ++hq)",
+                             "for (int64_t hq = h * group; hq < h * group + 1; ++hq)"),
     "attn_pool_divisor": ("out[d] = acc / (double)(t1 - t0);", "out[d] = acc / (double)ATTN_BLK;"),
     "attn_diag_block_dropped": ("                take[i] = 1;\n", "                take[i - 1] = 1;\n"),
     "kv3_sum_not_squared": ("for (int i = 0; i < D; ++i) v[i] = y[i] * y[i];",
