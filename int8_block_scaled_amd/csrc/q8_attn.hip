@@ -11,22 +11,24 @@
 // per K/V head, shared by its group of query heads.
 //
 // The forward kernel is a FlashAttention forward pass over the listed key
-// blocks, on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16):
-//   - a workgroup owns one query block (64 queries) of one head, a wave 16
-//     queries; the key and value blocks pass through LDS, shared by the four
-//     waves;
+// blocks, on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16):
+//   - a workgroup owns one query block (64 queries) of up to four query
+//     heads of one K/V head's group, two waves of 32 queries per head; the
+//     heads share the group's list, so each K/V block passes through LDS once
+//     for all of them;
 //   - scores are formed transposed, S^T = K Q^T, so that a lane owns one
-//     query (lane % 16) and four keys per 16-key tile: the running maximum
-//     and sum of the online softmax are per lane, and the exponentials in
-//     bf16 are already the B operand of the next product;
-//   - the output is formed transposed too, O^T = V^T P^T; the MFMA's 32-wide
-//     reduction index runs over keys in the order the score tiles hold them
-//     (lane group g supplies keys 4g..4g+3 of two consecutive 16-key tiles),
-//     and the V^T operand is read from LDS in the same order;
-//   - V is written to LDS transposed ([d][key]); rows, including those past
-//     the sequence end, come through range-checked buffer loads (zeros past
-//     L); LDS rows are padded so that the 16 lanes of each operand read hit
-//     distinct banks.
+//     query (lane % 32) and 16 keys per 32-key tile: the running maximum and
+//     sum of the online softmax are per lane (two lanes per query), and the
+//     exponentials in bf16 are already the B operand of the next product;
+//   - the output is formed transposed too, O^T = V^T P^T; the MFMA's 16-wide
+//     reduction index runs over keys in the order the score tiles hold them,
+//     and the V^T operand comes from row-major V in LDS through transposing
+//     reads (ds_read_b64_tr_b16), so K and V are staged alike;
+//   - K and V rows, including those past the sequence end, come through
+//     range-checked buffer loads (zeros past L) into two LDS buffers (one
+//     block attended while the next is stored), rows of 256 bytes with
+//     XOR-permuted 16-byte chunks, so both operand reads are free of bank
+//     conflicts.
 // The softmax runs in base 2: scores are scaled by log2(e)/sqrt(D) and
 // exponentiated with exp2 (v_exp_f32; a result below 2^-126 of the row's
 // maximum term flushes to zero, which no output can resolve).  The running
@@ -175,63 +177,73 @@ __global__ __launch_bounds__(kSelThreads) void attn_select_kernel(
 
 // ---------------------------------------------------------------- forward
 
-template <int D>
-struct FwdLds {
-  static constexpr int kKPitch = D + 8;          // bf16 per K row (272 bytes at D = 128)
-  static constexpr int kVPitch = kBlk + 8;       // bf16 per V^T row (144 bytes)
-  uint16_t k[kBlk * kKPitch];
-  uint16_t vt[D * kVPitch];
-};
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-template <int D, bool kBf16Out>
-__global__ __launch_bounds__(256, 3) void attn_fwd_kernel(
+constexpr int kRowBytes = 256;                  // LDS bytes per K or V row (D <= 128)
+constexpr int kTileBytes = kBlk * kRowBytes;    // one K or V block: 16 KB
+
+// LDS position of 16-byte chunk ch of row r of a K or V block: rows of 256
+// bytes, chunks permuted by an XOR of the row's low four bits, which spreads
+// both operand reads below (16-byte rows of K, 8-byte transposed pieces of
+// V) over the banks.
+__device__ __forceinline__ uint32_t lds_off(int r, int ch) {
+  const int sw = ((r & 3) << 2) ^ ((r >> 2) & 3);
+  return static_cast<uint32_t>(r * kRowBytes + 16 * (ch ^ sw));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), bf2));
+}
+
+// A workgroup owns query block i of GH query heads of K/V head g's group,
+// two waves of 32 queries per head; all read the same listed K/V blocks.
+template <int D, int GH, bool kBf16Out>
+__global__ __launch_bounds__(128 * GH, GH == 4 ? 2 : 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int64_t L, int64_t ldq, int64_t ldk, int64_t ldv, int64_t Hq, int64_t Hkv, int64_t NB,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int kmax,
     void* __restrict__ out, int64_t ldo, float scale_log2) {
-  using Lds = FwdLds<D>;
-  __shared__ Lds lds;
-  constexpr int KC = D / 32;                     // 32-wide d chunks of a score product
-  constexpr int DT = D / 16;                     // 16-row d tiles of the output
-  // Tiles (query block i, K/V head g), later blocks first (they list the
-  // most key blocks); the G = Hq/Hkv query heads of a tile share its list,
-  // so their workgroups are given ids 8 apart: workgroups are dealt to the
-  // 8 XCDs in turn, so the G of them run together on one XCD and read the
-  // listed K/V blocks through its L2.
-  const int64_t wg = blockIdx.x, G = Hq / Hkv, tiles = NB * Hkv;
-  int64_t t, hh;
-  if (tiles % 8 == 0) {
-    const int64_t x = wg % 8, y = wg / 8;
-    hh = y % G;
-    t = (y / G) * 8 + x;
-  } else {
-    t = wg / G;
-    hh = wg % G;
-  }
-  const int64_t i = NB - 1 - t / Hkv, g = t % Hkv, h = g * G + hh;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
-  const int64_t q0 = i * kBlk + 16 * wave;       // the wave's first query
-  const int64_t q = q0 + c;                      // this lane's query
+  constexpr int kThreads = 128 * GH;
+  constexpr int KS = D / 16;                     // 16-wide d steps of a score product
+  constexpr int DT = D / 32;                     // 32-row d tiles of the output
+  constexpr int kRowChunks = D / 8;              // 16-byte chunks per K or V row
+  constexpr int kPer = kBlk * kRowChunks / kThreads;   // chunks per thread and block
+  static_assert(kBlk * kRowChunks % kThreads == 0, "whole chunks per thread");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * kTileBytes];   // 2 x (K, V)
 
-  // Q^T operand: lane holds Q[q][32 kc + 8 gq .. +8] for every chunk kc
-  bf8 qb[KC];
+  // Tiles (K/V head g, query block i, head part), later blocks first within
+  // a head.  Workgroups are dealt to the 8 XCDs in turn; the order below
+  // gives each XCD a contiguous run of tiles, so that the query blocks of
+  // one K/V head, whose lists overlap, share that XCD's L2.
+  const int64_t G = Hq / Hkv, parts = G / GH, per_head = NB * parts, tiles = Hkv * per_head;
+  const int64_t wg = blockIdx.x;
+  const int64_t T = tiles % 8 == 0 ? (wg % 8) * (tiles / 8) + wg / 8 : wg;
+  const int64_t g = T / per_head, rem = T % per_head;
+  const int64_t i = NB - 1 - rem / parts, part = rem % parts;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, hb = lane >> 5;
+  const int64_t h = g * G + part * GH + wave / 2;
+  const int qh = wave & 1;
+  const int64_t q0 = i * kBlk + 32 * qh;         // the wave's first query
+
+  // Q^T operand: lane holds Q[q0 + c][16 ks + 8 hb .. +8] for every step ks
+  bf8 qb[KS];
   {
-    // rows of the wave's queries inside the sequence (none for a wave of the
-    // last, partial block that lies wholly past L)
-    const int64_t rows = L - q0 <= 0 ? 0 : (L - q0 < 16 ? L - q0 : 16);
+    const int64_t rows = L - q0 <= 0 ? 0 : (L - q0 < 32 ? L - q0 : 32);
     const __amdgpu_buffer_rsrc_t rq = rows_rsrc(Q + q0 * ldq + h * D, static_cast<uint32_t>(rows * ldq * 2));
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const v4u w = __builtin_amdgcn_raw_buffer_load_b128(
-          rq, static_cast<uint32_t>((c * ldq + 32 * kc + 8 * gq) * 2), 0, 0);
-      qb[kc] = __builtin_bit_cast(bf8, w);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      qb[ks] = __builtin_bit_cast(bf8, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rq, static_cast<uint32_t>((c * ldq + 16 * ks + 8 * hb) * 2), 0, 0));
   }
 
-  f4 o[DT];
+  f16v o[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f4{0, 0, 0, 0};
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f16v{};
   float m = -INFINITY, lsum = 0.0f;
 
   // the list is device data: clamp its length and skip entries outside the
@@ -240,7 +252,6 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(
   const int n_raw = cnt[g * NB + i];
   const int n = n_raw < 0 ? 0 : (n_raw > kmax ? kmax : n_raw);
   const int32_t* list = idx + (g * NB + i) * kmax;   // the K/V head's list
-  const int tid = threadIdx.x;
   auto next_valid = [&](int b) {                 // uniform
     for (; b < n; ++b) {
       const int32_t j = list[b];
@@ -249,90 +260,66 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(
     return b;
   };
 
-  // Global loads of a K/V block into registers, issued one block ahead.
-  // K: 16-byte chunks, row e / (D/8), column chunk e % (D/8).  V: a thread
-  // takes 4 consecutive keys (quad kq = e % 16) x 8 columns (octet
-  // dc = e / 16), so that its transposed 8-byte writes to LDS fall on
-  // distinct banks across 32 lanes.
-  constexpr int kKPer = kBlk * D / 8 / 256;      // K chunks per thread
-  constexpr int kVGroups = (kBlk / 4) * (D / 8); // (key quad, column octet) pairs
-  static_assert(kVGroups <= 256, "one V group per thread");
-  v4u kreg[kKPer], vreg[4];
+  // K and V blocks: 16-byte chunks through registers into LDS, row-major
+  // (rows past L read as zeros).
+  v4u kreg[kPer], vreg[kPer];
   auto load_block = [&](int64_t j) {
     const int64_t rows = L - j * kBlk < kBlk ? L - j * kBlk : kBlk;
     const __amdgpu_buffer_rsrc_t rk = rows_rsrc(K + j * kBlk * ldk + g * D, static_cast<uint32_t>(rows * ldk * 2));
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(V + j * kBlk * ldv + g * D, static_cast<uint32_t>(rows * ldv * 2));
 #pragma unroll
-    for (int u = 0; u < kKPer; ++u) {
-      const int e = u * 256 + tid, row = e / (D / 8), cc = e % (D / 8);
-      kreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, static_cast<uint32_t>((row * ldk + 8 * cc) * 2), 0, 0);
-    }
-    if (tid < kVGroups) {
-      const __amdgpu_buffer_rsrc_t rv = rows_rsrc(V + j * kBlk * ldv + g * D, static_cast<uint32_t>(rows * ldv * 2));
-      const int kq = tid % 16, dc = tid / 16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(
-            rv, static_cast<uint32_t>(((4 * kq + r) * ldv + 8 * dc) * 2), 0, 0);
+    for (int u = 0; u < kPer; ++u) {
+      const int e = u * kThreads + tid, r = e / kRowChunks, ch = e % kRowChunks;
+      kreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, static_cast<uint32_t>((r * ldk + 8 * ch) * 2), 0, 0);
+      vreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<uint32_t>((r * ldv + 8 * ch) * 2), 0, 0);
     }
   };
-  auto store_block = [&]() {
+  auto store_block = [&](int buf) {
+    uint8_t* kt = lds + buf * 2 * kTileBytes;
+    uint8_t* vt = kt + kTileBytes;
 #pragma unroll
-    for (int u = 0; u < kKPer; ++u) {
-      const int e = u * 256 + tid, row = e / (D / 8), cc = e % (D / 8);
-      *reinterpret_cast<v4u*>(&lds.k[row * Lds::kKPitch + 8 * cc]) = kreg[u];
-    }
-    if (tid < kVGroups) {
-      const int kq = tid % 16, dc = tid / 16;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // columns 8dc + 2w (low halves) and 8dc + 2w + 1 (high halves)
-        const uint32_t lo01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
-        *reinterpret_cast<v2u*>(&lds.vt[(8 * dc + 2 * w) * Lds::kVPitch + 4 * kq]) = v2u{lo01, lo23};
-        *reinterpret_cast<v2u*>(&lds.vt[(8 * dc + 2 * w + 1) * Lds::kVPitch + 4 * kq]) = v2u{hi01, hi23};
-      }
+    for (int u = 0; u < kPer; ++u) {
+      const int e = u * kThreads + tid, r = e / kRowChunks, ch = e % kRowChunks;
+      *reinterpret_cast<v4u*>(kt + lds_off(r, ch)) = kreg[u];
+      *reinterpret_cast<v4u*>(vt + lds_off(r, ch)) = vreg[u];
     }
   };
 
-  int bi = next_valid(0);
-  if (bi < n) load_block(list[bi]);
-  while (bi < n) {
-    const int64_t j = list[bi];
-    __syncthreads();                             // the previous block's LDS reads are done
-    store_block();
-    __syncthreads();
-    bi = next_valid(bi + 1);
-    if (bi < n) load_block(list[bi]);            // in flight during this block's products
+  // this lane's source row and column for the transposed V reads: lane
+  // group gl = lane / 16 reads keys 4 (gl / 2) + (lane % 16) / 4 (+8) of a
+  // 16-key step, columns 16 (gl % 2) + 4 (lane % 4) of a 32-column tile
+  const int gl = lane >> 4, vrow = 4 * (gl >> 1) + ((lane & 15) >> 2), vcol = 16 * (gl & 1) + 4 * (lane & 3);
 
-    // scores: s[kt][r] = S[key 16 kt + 4 gq + r][query c], scaled to base 2
-    f4 s[4];
+  auto attend = [&](int buf, int64_t j) {
+    const uint8_t* kt = lds + buf * 2 * kTileBytes;
+    const uint8_t* vt = kt + kTileBytes;
+    // scores: s[t][4 jj + r] = S[key 32 t + 8 jj + 4 hb + r][query c]
+    f16v s[2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      f4 acc = {0, 0, 0, 0};
+    for (int t = 0; t < 2; ++t) {
+      f16v acc = {};
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const bf8 a = *reinterpret_cast<const bf8*>(&lds.k[(16 * kt + c) * Lds::kKPitch + 32 * kc + 8 * gq]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[kc], acc, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf8 a = *reinterpret_cast<const bf8*>(kt + lds_off(32 * t + c, 2 * ks + hb));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], acc, 0, 0, 0);
       }
-      s[kt] = acc;
+      s[t] = acc;
     }
     // causal mask, in the diagonal block only (uniform branch)
     if (j == i) {
-      const int qi = static_cast<int>(q - i * kBlk);   // query's row in the block
+      const int qi = 32 * qh + c;                // query's row in the block
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (16 * kt + 4 * gq + r > qi) s[kt][r] = -INFINITY;
+        for (int v = 0; v < 16; ++v)
+          if (32 * t + 8 * (v >> 2) + 4 * hb + (v & 3) > qi) s[t][v] = -INFINITY;
     }
-    // row maximum over the block's keys (4 lanes share a query), in base 2
+    // row maximum over the block's keys (lanes c and c + 32 share a query)
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-      mx = fmaxf(fmaxf(mx, fmaxf(s[kt][0], s[kt][1])), fmaxf(s[kt][2], s[kt][3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[t][v], s[t][v + 1]));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     mx *= scale_log2;
     // Lazy rescaling: the reference maximum m only moves when a block's
@@ -349,61 +336,83 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(
     }
     // p = 2^(s * log2(e)/sqrt(D) - m); this lane's part of the row sum
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], scale_log2, -m));
-        s[kt][r] = p;
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][v], scale_log2, -m));
+        s[t][v] = p;
         lsum += p;
       }
-
-    // O^T += V^T P^T, two 32-key chunks: slots 8 gq .. 8 gq + 3 are keys
-    // 32 pc + 4 gq + r (tile 2 pc), slots 8 gq + 4 .. + 7 keys 32 pc + 16 + 4 gq + r
+    // O^T += V^T P^T in 16-key steps (t, p2): slots 8 hb .. 8 hb + 3 are keys
+    // 32 t + 16 p2 + 4 hb + r, slots 8 hb + 4 .. + 7 the same + 8, which is
+    // where the score tile holds them (s[t][8 p2 .. 8 p2 + 7])
 #pragma unroll
-    for (int pc = 0; pc < 2; ++pc) {
-      typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-      typedef float f2 __attribute__((ext_vector_type(2)));
-      const bf2 p01 = __builtin_convertvector((f2{s[2 * pc][0], s[2 * pc][1]}), bf2);
-      const bf2 p23 = __builtin_convertvector((f2{s[2 * pc][2], s[2 * pc][3]}), bf2);
-      const bf2 p45 = __builtin_convertvector((f2{s[2 * pc + 1][0], s[2 * pc + 1][1]}), bf2);
-      const bf2 p67 = __builtin_convertvector((f2{s[2 * pc + 1][2], s[2 * pc + 1][3]}), bf2);
-      const v4u pw = {__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23),
-                      __builtin_bit_cast(uint32_t, p45), __builtin_bit_cast(uint32_t, p67)};
-      const bf8 pb = __builtin_bit_cast(bf8, pw);
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vr = &lds.vt[(16 * dt + c) * Lds::kVPitch + 32 * pc + 4 * gq];
-        const v2u lo = *reinterpret_cast<const v2u*>(vr);
-        const v2u hi = *reinterpret_cast<const v2u*>(vr + 16);
-        const v4u aw = {lo[0], lo[1], hi[0], hi[1]};
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, aw), pb, o[dt], 0, 0, 0);
+      for (int p2 = 0; p2 < 2; ++p2) {
+        const v4u pw = {pack_bf16(s[t][8 * p2], s[t][8 * p2 + 1]), pack_bf16(s[t][8 * p2 + 2], s[t][8 * p2 + 3]),
+                        pack_bf16(s[t][8 * p2 + 4], s[t][8 * p2 + 5]), pack_bf16(s[t][8 * p2 + 6], s[t][8 * p2 + 7])};
+        const bf8 pb = __builtin_bit_cast(bf8, pw);
+        const int r0 = 32 * t + 16 * p2 + vrow;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int col = 32 * dt + vcol;
+          const uint32_t off = (col & 4) * 2;    // 8-byte half of the 16-byte chunk
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4s*)(vt + lds_off(r0, col >> 3) + off));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4s*)(vt + lds_off(r0 + 8, col >> 3) + off));
+          const v4u aw = {__builtin_bit_cast(v2u, lo)[0], __builtin_bit_cast(v2u, lo)[1],
+                          __builtin_bit_cast(v2u, hi)[0], __builtin_bit_cast(v2u, hi)[1]};
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8, aw), pb, o[dt], 0, 0, 0);
+        }
       }
+  };
+
+  // Two LDS buffers: while block b is attended from one, block b+1 (loaded
+  // into registers during block b-1) is stored into the other and block b+2
+  // is loaded; one barrier per block.
+  int cur = next_valid(0);
+  int nxt = cur < n ? next_valid(cur + 1) : n;
+  if (cur < n) {
+    load_block(list[cur]);
+    store_block(0);
+  }
+  if (nxt < n) load_block(list[nxt]);
+  __syncthreads();
+  int buf = 0;
+  while (cur < n) {
+    attend(buf, list[cur]);
+    int nn = n;
+    if (nxt < n) {
+      store_block(buf ^ 1);
+      nn = next_valid(nxt + 1);
+      if (nn < n) load_block(list[nn]);
     }
+    __syncthreads();
+    cur = nxt;
+    nxt = nn;
+    buf ^= 1;
   }
 
-  // the 4 lanes of a query hold parts of its row sum
-  lsum += __shfl_xor(lsum, 16);
+  // lanes c and c + 32 hold parts of the query's row sum
   lsum += __shfl_xor(lsum, 32);
-  // O[q][h*D + 16 dt + 4 gq + r] = o[dt][r] / lsum
+  // O[q][h*D + 32 dt + 8 jj + 4 hb + r] = o[dt][4 jj + r] / lsum
+  const int64_t q = q0 + c;
   if (q < L) {
     const float inv = 1.0f / lsum;
-    if constexpr (kBf16Out) {
-      uint16_t* orow = static_cast<uint16_t*>(out) + q * ldo + h * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-        typedef float f2 __attribute__((ext_vector_type(2)));
-        const bf2 a = __builtin_convertvector((f2{o[dt][0] * inv, o[dt][1] * inv}), bf2);
-        const bf2 b = __builtin_convertvector((f2{o[dt][2] * inv, o[dt][3] * inv}), bf2);
-        *reinterpret_cast<v2u*>(orow + 16 * dt + 4 * gq) =
-            v2u{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t col = h * D + 32 * dt + 8 * jj + 4 * hb;
+        const float a0 = o[dt][4 * jj] * inv, a1 = o[dt][4 * jj + 1] * inv;
+        const float a2 = o[dt][4 * jj + 2] * inv, a3 = o[dt][4 * jj + 3] * inv;
+        if constexpr (kBf16Out)
+          *reinterpret_cast<v2u*>(static_cast<uint16_t*>(out) + q * ldo + col) = v2u{pack_bf16(a0, a1), pack_bf16(a2, a3)};
+        else
+          *reinterpret_cast<f4*>(static_cast<float*>(out) + q * ldo + col) = f4{a0, a1, a2, a3};
       }
-    } else {
-      float* orow = static_cast<float*>(out) + q * ldo + h * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<f4*>(orow + 16 * dt + 4 * gq) = o[dt] * inv;
-    }
   }
 }
 
@@ -439,18 +448,27 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const int32_t* idx, const int32_t* cnt, int kmax, int out_dtype,
                            void* out, int64_t ldo, hipStream_t stream) {
   const int64_t NB = (L + kBlk - 1) / kBlk;
-  const uint32_t grid = static_cast<uint32_t>(Hq * NB);
+  const int64_t G = Hq / Hkv;
+  const int gh = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);   // query heads per workgroup
+  const uint32_t grid = static_cast<uint32_t>(Hq / gh * NB);
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
-#define Q8_ATTN_LAUNCH(DD, BF)                                                                   \
-  hipLaunchKernelGGL((attn_fwd_kernel<DD, BF>), dim3(grid), dim3(256), 0, stream, q, k, v, L, ldq, \
-                     ldk, ldv, Hq, Hkv, NB, idx, cnt, kmax, out, ldo, scale_log2)
+#define Q8_ATTN_LAUNCH(DD, GG, BF)                                                                \
+  hipLaunchKernelGGL((attn_fwd_kernel<DD, GG, BF>), dim3(grid), dim3(128 * GG), 0, stream, q, k, v, \
+                     L, ldq, ldk, ldv, Hq, Hkv, NB, idx, cnt, kmax, out, ldo, scale_log2)
+#define Q8_ATTN_GH(DD, BF)                \
+  do {                                    \
+    if (gh == 4) Q8_ATTN_LAUNCH(DD, 4, BF); \
+    else if (gh == 2) Q8_ATTN_LAUNCH(DD, 2, BF); \
+    else Q8_ATTN_LAUNCH(DD, 1, BF);       \
+  } while (0)
   if (D == 128) {
-    if (out_dtype == 1) Q8_ATTN_LAUNCH(128, true);
-    else Q8_ATTN_LAUNCH(128, false);
+    if (out_dtype == 1) Q8_ATTN_GH(128, true);
+    else Q8_ATTN_GH(128, false);
   } else {
-    if (out_dtype == 1) Q8_ATTN_LAUNCH(64, true);
-    else Q8_ATTN_LAUNCH(64, false);
+    if (out_dtype == 1) Q8_ATTN_GH(64, true);
+    else Q8_ATTN_GH(64, false);
   }
+#undef Q8_ATTN_GH
 #undef Q8_ATTN_LAUNCH
   return hipGetLastError();
 }
