@@ -26,9 +26,8 @@
 //     reads (ds_read_b64_tr_b16), so K and V are staged alike;
 //   - K and V rows, including those past the sequence end, come through
 //     range-checked buffer loads (zeros past L) into two LDS buffers (one
-//     block attended while the next is stored), rows of 256 bytes with
-//     XOR-permuted 16-byte chunks, so both operand reads are free of bank
-//     conflicts.
+//     block attended while the next is stored), with rows padded so that
+//     both operand reads are nearly free of bank conflicts.
 // The softmax runs in base 2: scores are scaled by log2(e)/sqrt(D) and
 // exponentiated with exp2 (v_exp_f32; a result below 2^-126 of the row's
 // maximum term flushes to zero, which no output can resolve).  The running
@@ -183,17 +182,13 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-constexpr int kRowBytes = 256;                  // LDS bytes per K or V row (D <= 128)
-constexpr int kTileBytes = kBlk * kRowBytes;    // one K or V block: 16 KB
-
-// LDS position of 16-byte chunk ch of row r of a K or V block: rows of 256
-// bytes, chunks permuted by an XOR of the row's low four bits, which spreads
-// both operand reads below (16-byte rows of K, 8-byte transposed pieces of
-// V) over the banks.
-__device__ __forceinline__ uint32_t lds_off(int r, int ch) {
-  const int sw = ((r & 3) << 2) ^ ((r >> 2) & 3);
-  return static_cast<uint32_t>(r * kRowBytes + 16 * (ch ^ sw));
-}
+// LDS rows of a K or V block (D <= 128), padded so that the operand reads
+// spread over the banks: K rows of 272 bytes for the 16-byte reads of 32 rows
+// x 2 chunks, V rows of 288 bytes for the transposing 8-byte reads of 8 rows
+// x 64 bytes.  Every read is a per-lane base plus a constant offset.
+constexpr int kKPitch = 272, kVPitch = 288;
+constexpr int kKTile = kBlk * kKPitch, kVTile = kBlk * kVPitch;
+constexpr int kBlockBytes = kKTile + kVTile;   // one resident block: 35 KB
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), bf2));
@@ -213,7 +208,7 @@ __global__ __launch_bounds__(128 * GH, GH == 4 ? 2 : 1) void attn_fwd_kernel(
   constexpr int kRowChunks = D / 8;              // 16-byte chunks per K or V row
   constexpr int kPer = kBlk * kRowChunks / kThreads;   // chunks per thread and block
   static_assert(kBlk * kRowChunks % kThreads == 0, "whole chunks per thread");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * kTileBytes];   // 2 x (K, V)
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBlockBytes];   // 2 x (K, V)
 
   // Tiles (K/V head g, query block i, head part), later blocks first within
   // a head.  Workgroups are dealt to the 8 XCDs in turn; the order below
@@ -275,13 +270,13 @@ __global__ __launch_bounds__(128 * GH, GH == 4 ? 2 : 1) void attn_fwd_kernel(
     }
   };
   auto store_block = [&](int buf) {
-    uint8_t* kt = lds + buf * 2 * kTileBytes;
-    uint8_t* vt = kt + kTileBytes;
+    uint8_t* kt = lds + buf * kBlockBytes;
+    uint8_t* vt = kt + kKTile;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int e = u * kThreads + tid, r = e / kRowChunks, ch = e % kRowChunks;
-      *reinterpret_cast<v4u*>(kt + lds_off(r, ch)) = kreg[u];
-      *reinterpret_cast<v4u*>(vt + lds_off(r, ch)) = vreg[u];
+      *reinterpret_cast<v4u*>(kt + r * kKPitch + 16 * ch) = kreg[u];
+      *reinterpret_cast<v4u*>(vt + r * kVPitch + 16 * ch) = vreg[u];
     }
   };
 
@@ -290,9 +285,11 @@ __global__ __launch_bounds__(128 * GH, GH == 4 ? 2 : 1) void attn_fwd_kernel(
   // 16-key step, columns 16 (gl % 2) + 4 (lane % 4) of a 32-column tile
   const int gl = lane >> 4, vrow = 4 * (gl >> 1) + ((lane & 15) >> 2), vcol = 16 * (gl & 1) + 4 * (lane & 3);
 
+  const uint32_t k_off = static_cast<uint32_t>(c * kKPitch + 16 * hb);
+  const uint32_t v_off = static_cast<uint32_t>(kKTile + vrow * kVPitch + 2 * vcol);
   auto attend = [&](int buf, int64_t j) {
-    const uint8_t* kt = lds + buf * 2 * kTileBytes;
-    const uint8_t* vt = kt + kTileBytes;
+    const uint8_t* kt = lds + buf * kBlockBytes + k_off;
+    const uint8_t* vt = lds + buf * kBlockBytes + v_off;
     // scores: s[t][4 jj + r] = S[key 32 t + 8 jj + 4 hb + r][query c]
     f16v s[2];
 #pragma unroll
@@ -300,7 +297,7 @@ __global__ __launch_bounds__(128 * GH, GH == 4 ? 2 : 1) void attn_fwd_kernel(
       f16v acc = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf8 a = *reinterpret_cast<const bf8*>(kt + lds_off(32 * t + c, 2 * ks + hb));
+        const bf8 a = *reinterpret_cast<const bf8*>(kt + 32 * t * kKPitch + 32 * ks);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], acc, 0, 0, 0);
       }
       s[t] = acc;
@@ -319,7 +316,7 @@ __global__ __launch_bounds__(128 * GH, GH == 4 ? 2 : 1) void attn_fwd_kernel(
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[t][v], s[t][v + 1]));
+      for (int v = 0; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s[t][v]), s[t][v + 1]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     mx *= scale_log2;
     // Lazy rescaling: the reference maximum m only moves when a block's
@@ -353,15 +350,11 @@ __global__ __launch_bounds__(128 * GH, GH == 4 ? 2 : 1) void attn_fwd_kernel(
         const v4u pw = {pack_bf16(s[t][8 * p2], s[t][8 * p2 + 1]), pack_bf16(s[t][8 * p2 + 2], s[t][8 * p2 + 3]),
                         pack_bf16(s[t][8 * p2 + 4], s[t][8 * p2 + 5]), pack_bf16(s[t][8 * p2 + 6], s[t][8 * p2 + 7])};
         const bf8 pb = __builtin_bit_cast(bf8, pw);
-        const int r0 = 32 * t + 16 * p2 + vrow;
+        const int r0 = 32 * t + 16 * p2;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int col = 32 * dt + vcol;
-          const uint32_t off = (col & 4) * 2;    // 8-byte half of the 16-byte chunk
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4s*)(vt + lds_off(r0, col >> 3) + off));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4s*)(vt + lds_off(r0 + 8, col >> 3) + off));
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + r0 * kVPitch + 64 * dt));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vt + (r0 + 8) * kVPitch + 64 * dt));
           const v4u aw = {__builtin_bit_cast(v2u, lo)[0], __builtin_bit_cast(v2u, lo)[1],
                           __builtin_bit_cast(v2u, hi)[0], __builtin_bit_cast(v2u, hi)[1]};
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8, aw), pb, o[dt], 0, 0, 0);
