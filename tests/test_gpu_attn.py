@@ -121,7 +121,11 @@ def test_attn_select(orc, L, Hq, Hkv, D, k):
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("L,Hq,Hkv,D,k", [(64, 2, 1, 64, 2), (100, 4, 2, 128, 2),
                                           (640, 4, 2, 64, 4), (1111, 2, 2, 128, 5),
-                                          (1000, 8, 2, 128, 100), (777, 4, 4, 64, 3)])
+                                          (1000, 8, 2, 128, 100), (777, 4, 4, 64, 3),
+                                          # groups of 8, 6 and 3 query heads: a group
+                                          # spans 2 or 3 workgroups of 4, 2 or 1 heads
+                                          (500, 16, 2, 128, 4), (300, 12, 2, 64, 3),
+                                          (257, 9, 3, 128, 2)])
 def test_attn_fwd(orc, L, Hq, Hkv, D, k, out_dtype):
     """The oracle's lists fed to the kernel; output within the bar."""
     qb, kb, vb, qt, kt, vt = _run(orc, L, Hq, Hkv, D, k, 50 + L % 97)
