@@ -88,21 +88,34 @@ __global__ __launch_bounds__(256) void attn_pool_kernel(const uint16_t* __restri
 constexpr int kSelThreads = 256;
 constexpr int kMaxBlocks = 4096;               // 256K tokens
 
+// Order-preserving map of a binary32 score to 32 bits (larger score, larger
+// key); -0 is first made +0, so equal scores give equal keys.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // One workgroup per (K/V head g, query block i): scores of blocks 0 < j < i,
-// the sum of the group's pooled query rows against the pooled key rows, a
-// bitonic sort by (score descending, block ascending), then block 0, block
-// i and the first (k - 2) of the sort, written in ascending order.
+// the sum of the group's pooled query rows against the pooled key rows; the
+// (k-2)'th largest score is found by a radix select over the score keys
+// (four 8-bit digits, a histogram each), then every block scoring above it
+// is taken, and of those scoring equal to it the lowest blocks, as many as
+// complete k - 2 -- the first k - 2 of the order (score descending, block
+// ascending).  Block 0 and block i are added, and the list is written in
+// ascending order.
 template <int D>
 __global__ __launch_bounds__(kSelThreads) void attn_select_kernel(
     const float* __restrict__ pq, const float* __restrict__ pk, int64_t Hq, int64_t Hkv,
     int64_t NB, int k, int kmax, int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
-  __shared__ float sc[kMaxBlocks];
-  __shared__ int32_t id[kMaxBlocks];
+  static_assert(kSelThreads == 256, "one histogram bin per thread");
+  __shared__ uint32_t key[kMaxBlocks];
   __shared__ uint8_t take[kMaxBlocks];
-  __shared__ float qrow[D];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sel[2];
+  __shared__ __attribute__((aligned(16))) float qrow[D];
   const int64_t g = blockIdx.x / NB, i = blockIdx.x % NB;
   const int64_t G = Hq / Hkv;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   int32_t* out = idx + (g * NB + i) * kmax;
   for (int m = tid; m < kmax; m += kSelThreads) out[m] = -1;
   for (int64_t j = tid; j <= i; j += kSelThreads) take[j] = (k >= i + 1 || j == 0 || j == i) ? 1 : 0;
@@ -114,49 +127,88 @@ __global__ __launch_bounds__(kSelThreads) void attn_select_kernel(
       qrow[d] = a;
     }
     __syncthreads();
-    // candidates 1 .. i-1, padded to a power of two with -inf
+    // candidates e = j - 1 for j = 1 .. i-1: eight lanes per candidate row,
+    // each reading 16-byte pieces 16 (p + 8 k) of it, so that a wave's load
+    // covers eight whole 128-byte lines; the eight partial sums are added
+    // across the lanes
     const int ncand = static_cast<int>(i - 1);
-    int n2 = 1;
-    while (n2 < ncand) n2 <<= 1;
-    for (int e = tid; e < n2; e += kSelThreads) {
-      float s = -INFINITY;
-      const int j = e + 1;
-      if (e < ncand) {
-        const float4* kr = reinterpret_cast<const float4*>(pk + (g * NB + j) * D);
+    {
+      const int rs = lane >> 3, pp = lane & 7;
+      const int w = tid >> 6;
+      for (int e0 = 8 * w; e0 < ncand; e0 += 8 * (kSelThreads / 64)) {
+        const int e = e0 + rs;
+        const float4* kr = reinterpret_cast<const float4*>(pk + (g * NB + (e < ncand ? e + 1 : 1)) * D);
         float a = 0.0f;
-#pragma unroll 4
-        for (int d4 = 0; d4 < D / 4; ++d4) {
+#pragma unroll
+        for (int k4 = 0; k4 < D / 32; ++k4) {
+          const int d4 = pp + 8 * k4;
           const float4 kv = kr[d4];
-          a += qrow[4 * d4] * kv.x;
-          a += qrow[4 * d4 + 1] * kv.y;
-          a += qrow[4 * d4 + 2] * kv.z;
-          a += qrow[4 * d4 + 3] * kv.w;
+          const float4 qv = *reinterpret_cast<const float4*>(&qrow[4 * d4]);
+          a += qv.x * kv.x;
+          a += qv.y * kv.y;
+          a += qv.z * kv.z;
+          a += qv.w * kv.w;
         }
-        s = a;
+        a += __shfl_xor(a, 4);
+        a += __shfl_xor(a, 2);
+        a += __shfl_xor(a, 1);
+        if (pp == 0 && e < ncand) key[e] = score_key(a);
       }
-      sc[e] = s;
-      id[e] = e < ncand ? j : 0x7fffffff;
     }
     __syncthreads();
-    // bitonic sort, "before" = higher score, then lower block
-    for (int size = 2; size <= n2; size <<= 1)
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int e = tid; e < n2 / 2; e += kSelThreads) {
-          const int lo = 2 * e - (e & (stride - 1)), hi = lo + stride;
-          const bool up = (lo & size) == 0;         // this run sorts "before"-first
-          const float s0 = sc[lo], s1 = sc[hi];
-          const int32_t i0 = id[lo], i1 = id[hi];
-          const bool hi_first = s1 > s0 || (s1 == s0 && i1 < i0);
-          if (hi_first == up) {
-            sc[lo] = s1;
-            sc[hi] = s0;
-            id[lo] = i1;
-            id[hi] = i0;
-          }
-        }
-        __syncthreads();
+    // radix select of the want'th largest key, most significant digit first
+    uint32_t prefix = 0, pmask = 0;
+    int want = k - 2;                            // 1 <= want < ncand
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      hist[tid] = 0;
+      __syncthreads();
+      for (int e = tid; e < ncand; e += kSelThreads) {
+        const uint32_t u = key[e];
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
       }
-    for (int e = tid; e < k - 2; e += kSelThreads) take[id[e]] = 1;
+      __syncthreads();
+      if (tid < 64) {
+        // lane l holds bins 4l .. 4l+3; counts above them from a suffix scan
+        const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
+        const uint32_t t = c0 + c1 + c2 + c3;
+        uint32_t x = t;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_down(x, off);
+          if (lane + off < 64) x += y;
+        }
+        uint32_t cum = x - t;                    // keys in bins above 4l+3
+        const uint32_t cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+        for (int q = 3; q >= 0; --q) {
+          if (cum < static_cast<uint32_t>(want) && cum + cs[q] >= static_cast<uint32_t>(want)) {
+            sel[0] = static_cast<uint32_t>(4 * lane + q);
+            sel[1] = static_cast<uint32_t>(want) - cum;
+          }
+          cum += cs[q];
+        }
+      }
+      __syncthreads();
+      prefix |= sel[0] << shift;
+      pmask |= 255u << shift;
+      want = static_cast<int>(sel[1]);
+    }
+    // prefix is now the threshold key; want of the keys equal to it are taken
+    for (int e = tid; e < ncand; e += kSelThreads)
+      if (key[e] > prefix) take[e + 1] = 1;
+    if (tid < 64) {                              // the lowest blocks among the equal keys
+      int base = 0;
+      for (int e0 = 0; e0 < ncand && base < want; e0 += 64) {
+        const int e = e0 + lane;
+        const bool f = e < ncand && key[e] == prefix;
+        const uint64_t mask = __ballot(f);
+        const int rank = base + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                    static_cast<uint32_t>(mask >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0)));
+        if (f && rank < want) take[e + 1] = 1;
+        base += __popcll(mask);
+      }
+    }
   }
   __syncthreads();
   // compact ascending with the first wave
