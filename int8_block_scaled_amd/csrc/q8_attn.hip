@@ -55,32 +55,35 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 // ------------------------------------------------------------------- pool
 
 // pooled[h][b][d] = mean of x[t][h*D + d] over the block's tokens (binary32,
-// summed in token order).  16 threads per (h, b), 8 columns each (D = 128;
-// 8 threads for D = 64).
-template <int D>
+// summed in token order).  A workgroup takes 256 16-byte column chunks of
+// one block (8 columns each, all heads side by side), so a wave's loads read
+// 1 KB of a token row.
 __global__ __launch_bounds__(256) void attn_pool_kernel(const uint16_t* __restrict__ x, int64_t L,
-                                                        int64_t ldx, int64_t H, int64_t NB,
-                                                        float* __restrict__ pooled) {
-  constexpr int kThr = D / 8;
-  const int64_t pair = static_cast<int64_t>(blockIdx.x) * (256 / kThr) + threadIdx.x / kThr;
-  if (pair >= H * NB) return;
-  const int c = threadIdx.x % kThr;
-  const int64_t h = pair / NB, b = pair % NB;
+                                                        int64_t ldx, int64_t H, int64_t D,
+                                                        int64_t NB, float* __restrict__ pooled) {
+  const int64_t chunks = H * D / 8;              // 16-byte chunks per token row
+  const int64_t groups = (chunks + 255) / 256;
+  const int64_t b = blockIdx.x / groups;
+  const int64_t cc = (blockIdx.x % groups) * 256 + threadIdx.x;
+  if (cc >= chunks) return;
   const int64_t t0 = b * kBlk, t1 = t0 + kBlk < L ? t0 + kBlk : L;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const uint16_t* src = x + 8 * cc;
+#pragma unroll 8
   for (int64_t t = t0; t < t1; ++t) {
-    const uint4 w = *reinterpret_cast<const uint4*>(x + t * ldx + h * D + 8 * c);
+    const uint4 w = *reinterpret_cast<const uint4*>(src + t * ldx);
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += bf16_to_f32(ww[i] & 0xffffu);
-      acc[2 * i + 1] += bf16_to_f32(ww[i] >> 16);
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += bf16_to_f32(ww[q] & 0xffffu);
+      acc[2 * q + 1] += bf16_to_f32(ww[q] >> 16);
     }
   }
   const float n = static_cast<float>(t1 - t0);
-  float* out = pooled + pair * D + 8 * c;
+  const int64_t h = cc / (D / 8), c8 = cc % (D / 8);
+  float* out = pooled + (h * NB + b) * D + 8 * c8;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) out[i] = acc[i] / n;
+  for (int q = 0; q < 8; ++q) out[q] = acc[q] / n;
 }
 
 // ----------------------------------------------------------------- select
@@ -466,12 +469,9 @@ __global__ __launch_bounds__(128 * GH, GH == 4 ? 2 : 1) void attn_fwd_kernel(
 hipError_t launch_attn_pool(const uint16_t* x, int64_t L, int64_t ldx, int64_t H, int64_t D,
                             float* pooled, hipStream_t stream) {
   const int64_t NB = (L + kBlk - 1) / kBlk;
-  const int64_t per = 256 / (D / 8);
-  const uint32_t grid = static_cast<uint32_t>((H * NB + per - 1) / per);
-  if (D == 128)
-    hipLaunchKernelGGL((attn_pool_kernel<128>), dim3(grid), dim3(256), 0, stream, x, L, ldx, H, NB, pooled);
-  else
-    hipLaunchKernelGGL((attn_pool_kernel<64>), dim3(grid), dim3(256), 0, stream, x, L, ldx, H, NB, pooled);
+  const int64_t groups = (H * D / 8 + 255) / 256;
+  const uint32_t grid = static_cast<uint32_t>(NB * groups);
+  hipLaunchKernelGGL(attn_pool_kernel, dim3(grid), dim3(256), 0, stream, x, L, ldx, H, D, NB, pooled);
   return hipGetLastError();
 }
 
