@@ -95,8 +95,8 @@ def main():
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
     if args.gpus != 1:
-        sys.exit("bench.py measures one GPU: this build has no multi-GPU path "
-                 "(the product shards by N or M with no communication; see DESIGN.md). "
+        sys.exit("bench.py measures one GPU: the library has no multi-GPU path "
+                 "(the product shards by N or M with no communication). "
                  "Run with --gpus 1.")
 
     import numpy as np
