@@ -22,10 +22,12 @@
 // i.e. two VALU operations per output and block, with no int->float
 // conversion.  d_w is per lane (lane = output column); the pair
 // (d_w, -1.5*2^23*d_w) is prepared once per block when staged (the product
-// is exact: d_w has 11 significant bits).  With unpacked binary32 FMAs (16
-// lanes per clock per SIMD) against 1024 int8 MACs per clock per SIMD, this
-// epilogue caps the kernel at 1/4 of the int8 matrix-core peak, so the
-// kernel is built to keep the VALU issuing epilogue FMAs and little else.
+// is exact: d_w has 11 significant bits).  Against 1024 int8 MACs per clock
+// per SIMD, 32 unpacked binary32 FMAs per 32-cycle MFMA tile cap the kernel
+// well below the matrix-core peak: a single wave issues an FMA every ~4.6
+// clocks, two waves of a SIMD together one every ~2.7 (measured), so the cap
+// lies between 1/4 and ~3/8 of the peak, and the kernel is built to keep the
+// VALU issuing epilogue FMAs and little else.
 //
 // Data movement.  A workgroup of WAVES_M x WAVES_N waves owns a BM x BN
 // output tile; K advances in stages of KBS blocks through two LDS buffers.
