@@ -40,7 +40,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Under C++ both enumerations have int as their fixed underlying type, so
+ * that any int a C caller passes is a value of the type: an unknown dtype is
+ * then rejected by the checks below (Q8_ERR_DTYPE), never undefined.  The
+ * layout is an int either way. */
+#ifdef __cplusplus
+#define Q8_ENUM_BASE : int
+#else
+#define Q8_ENUM_BASE
+#endif
+
+typedef enum q8_status_e Q8_ENUM_BASE {
     Q8_OK = 0,
     Q8_ERR_NULL = 1,    /* a required pointer is NULL                        */
     Q8_ERR_SHAPE = 2,   /* K < 32, K % 32 != 0, K > 2^24, N <= 0, M < 0,
@@ -52,7 +62,7 @@ typedef enum {
     Q8_ERR_LAUNCH = 7   /* the kernel launch was rejected by the runtime     */
 } q8_status;
 
-typedef enum {
+typedef enum q8_dtype_e Q8_ENUM_BASE {
     Q8_F32 = 0,         /* IEEE binary32                                     */
     Q8_BF16 = 1         /* bfloat16 (upper half of a binary32)               */
 } q8_dtype;
