@@ -73,11 +73,13 @@ constexpr int kBiasBits = 0x4B400000;           // its binary32 bits
 
 // MF: output tile of one MFMA, 32 (v_mfma_i32_32x32x32_i8) or 16
 // (v_mfma_i32_16x16x32_i8).
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int KBS_, int NBUF_, int MF_ = 32>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int KBS_, int NBUF_, int MF_ = 32,
+          int PIPE_ = 0>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, KBS = KBS_;
   static constexpr int NBUF = NBUF_;                           // LDS stage buffers
   static constexpr int MF = MF_;
+  static constexpr int PIPE = PIPE_;
   static constexpr int kAccN = MF * MF / 64;                   // accumulator values per lane and tile
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
   static constexpr int kWaves = WAVES_M * WAVES_N;
@@ -346,6 +348,22 @@ __device__ __forceinline__ void compute_stage(uint32_t base_a, uint32_t base_as,
         av[4 * q + 2] = __int_as_float(avq[i][q].z);
         av[4 * q + 3] = __int_as_float(avq[i][q].w);
       }
+      if constexpr (T::PIPE) {
+        // All of the row tile's MFMAs first: the later ones run on the matrix
+        // core while this wave applies the scales to the first.
+        v16i p[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          p[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], bias, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float y = fmaf(__int_as_float(p[j][r]), wp[j].x, wp[j].y);
+            acc[i][j][r] = fmaf(y, av[r], acc[i][j][r]);
+          }
+      } else {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], bias, 0, 0, 0);
@@ -354,6 +372,7 @@ __device__ __forceinline__ void compute_stage(uint32_t base_a, uint32_t base_as,
           const float y = fmaf(__int_as_float(p[r]), wp[j].x, wp[j].y);
           acc[i][j][r] = fmaf(y, av[r], acc[i][j][r]);
         }
+      }
       }
     }
     // Keep blocks apart: the block's accumulator updates complete before the
@@ -583,6 +602,12 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
     asm volatile("s_barrier" ::: "memory");
   }
   wait_vmcnt<0>();   // the loads issued past the end are done before LDS is released
+  {
+    // The lane's position again, from the hardware lane count rather than
+    // from values kept across the loop, whose registers it needs.
+    const int lane_o = static_cast<int>(
+        __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+    const int half = lane_o >> 5, l32 = lane_o & 31, g = lane_o >> 4, l16 = lane_o & 15;
 
   if constexpr (kSwiglu) {
     // The wave's 64 columns are one row group: column l32 is the gate of
@@ -622,6 +647,7 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
                             (T::MF == 32 ? 8 * (r >> 2) + 4 * half + (r & 3) : 4 * g + r);
         if (row < M) C[row * ldc + col] = acc[i][j][r];
       }
+  }
   }
 }
 
@@ -675,6 +701,7 @@ const TileConfig kTiles[] = {
     {64, 128, launch_tile<Tile<64, 128, 2, 2, 2, 2>, 4>},         // 1: 4 waves 32x64, KBS 2
     {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2, 16>, 4>},   // 2: as 0 on 16x16 MFMAs
     {128, 256, launch_tile<Tile<128, 256, 4, 4, 4, 2>, 4>},       // 3: 16 waves 32x64
+    {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2, 32, 1>, 4>},   // 4: as 0, MFMAs first
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -684,10 +711,11 @@ int pick_tile(int64_t M, int64_t N) {
     const int t = atoi(e);
     if (t >= 0 && t < kNumTiles) return t;
   }
-  // 128x128 tiles, unless that leaves CUs idle (fewer tiles than the 256
-  // CUs): then 64x128 tiles double the workgroup count.
+  // 128x128 tiles with a wave's MFMAs issued ahead of its epilogues, unless
+  // that leaves CUs idle (fewer tiles than the 256 CUs): then 64x128 tiles
+  // double the workgroup count.
   const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
-  return tiles128 < 256 ? 1 : 0;
+  return tiles128 < 256 ? 1 : 4;
 }
 
 }  // namespace
@@ -700,7 +728,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const
 hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a,
                               const uint16_t* d_a, const uint8_t* w_packed, int8_t* q_h,
                               uint16_t* d_h, hipStream_t stream) {
-  // The 32x32-MFMA tiles with 64-column wave tiles (0, 1 and 3) carry the
+  // The 32x32-MFMA tiles with 64-column wave tiles (0, 1, 3 and 4) carry the
   // epilogue; the 16x16 variant (2) is replaced by tile 0.
   const int64_t N = 2 * I;
   switch (pick_tile(M, N)) {
@@ -710,9 +738,13 @@ hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a
     case 3:
       return launch_tile_impl<Tile<128, 256, 4, 4, 4, 2>, 4, true>(M, N, K, q_a, d_a, w_packed,
                                                                    nullptr, N, stream, q_h, d_h);
-    default:
+    case 0:
+    case 2:
       return launch_tile_impl<Tile<128, 128, 4, 2, 4, 2>, 4, true>(M, N, K, q_a, d_a, w_packed,
                                                                    nullptr, N, stream, q_h, d_h);
+    default:
+      return launch_tile_impl<Tile<128, 128, 4, 2, 4, 2, 32, 1>, 4, true>(
+          M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
   }
 }
 
