@@ -73,16 +73,24 @@ constexpr int kBiasBits = 0x4B400000;           // its binary32 bits
 
 // MF: output tile of one MFMA, 32 (v_mfma_i32_32x32x32_i8) or 16
 // (v_mfma_i32_16x16x32_i8).
+// KSPLIT_ > 1: the workgroup's waves form KSPLIT groups of WAVES_M x
+// WAVES_N; group g computes blocks [g*KBS/KSPLIT, (g+1)*KBS/KSPLIT) of every
+// stage, and the groups' partial sums are added through LDS at the end, in
+// group order.  This gives grids with few output tiles (small M, narrow N)
+// several waves per SIMD.
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int KBS_, int NBUF_, int MF_ = 32,
-          int PIPE_ = 0>
+          int PIPE_ = 0, int KSPLIT_ = 1>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, KBS = KBS_;
   static constexpr int NBUF = NBUF_;                           // LDS stage buffers
   static constexpr int MF = MF_;
   static constexpr int PIPE = PIPE_;
+  static constexpr int KSPLIT = KSPLIT_;
+  static constexpr int NB = KBS / KSPLIT;                      // blocks per wave per stage
   static constexpr int kAccN = MF * MF / 64;                   // accumulator values per lane and tile
-  static constexpr int kThreads = WAVES_M * WAVES_N * 64;
-  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kWavesT = WAVES_M * WAVES_N;            // waves of one K group
+  static constexpr int kThreads = kWavesT * KSPLIT * 64;
+  static constexpr int kWaves = kWavesT * KSPLIT;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // per-wave tile
   static constexpr int TM = WM / MF, TN = WN / MF;             // MFMA tiles per wave
   static constexpr int kSlots = 2 * KBS;                       // 16-byte slots per row per stage
@@ -112,6 +120,9 @@ struct Tile {
   static constexpr int kInFlight = (NBUF - 1) * kScaleOps + (NBUF - 2) * kDmaOps;
   static_assert(kInFlight < 64, "vmcnt range");
   static_assert(kStage < 65536, "immediate LDS offsets");
+  static_assert(KBS % KSPLIT == 0 && (KSPLIT == 1 || MF == 32), "K groups");
+  // partial sums of groups 1.. go through the stage buffers
+  static_assert((KSPLIT - 1) * kWavesT * TM * TN * kAccN * 64 * 4 <= NBUF * kStage, "LDS");
 };
 
 // ---------------------------------------------------------------------------
@@ -307,7 +318,7 @@ __device__ __forceinline__ void compute_stage(uint32_t base_a, uint32_t base_as,
                                               uint32_t base_bs, const v16i& bias,
                                               v16f (&acc)[T::TM][T::TN], F&& at_block) {
   constexpr int TM = T::TM, TN = T::TN, BM = T::BM, BN = T::BN;
-  static_for<T::KBS>([&](auto kb_) __attribute__((always_inline)) {
+  static_for<T::NB>([&](auto kb_) __attribute__((always_inline)) {
     constexpr int kb = decltype(kb_)::value;
     v4i af[TM], avq[TM][4], bf[TN];
     v2f wp[TN];
@@ -528,20 +539,27 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   LaneOffsets<T> lo;
   lane_offsets<T>(lo, tid, wave, lane, static_cast<uint32_t>(K), static_cast<uint32_t>(KB));
 
-  const int wm0 = (wave % T::WAVES_M) * T::WM;
-  const int wn0 = (wave / T::WAVES_M) * T::WN;
+  const int kg = wave / T::kWavesT;              // K group
+  const int wt = wave % T::kWavesT;              // wave within the group's tile
+  const int wm0 = (wt % T::WAVES_M) * T::WM;
+  const int wn0 = (wt / T::WAVES_M) * T::WN;
+  const uint32_t kofs = static_cast<uint32_t>(kg * T::NB);   // group's first block in a stage
   const int half = lane >> 5;
   const int l32 = lane & 31;
   // lane parts of the LDS addresses read by compute_stage
   // (32x32: lane l reads row/column l%32, half l/32; 16x16: row/column
   // l%16, bytes 8*(l/16) .. +8 of the block, i.e. half g/2, offset 8*(g%2))
   const int g = lane >> 4, l16 = lane & 15;
-  const uint32_t lane_a = T::MF == 32 ? (half * BM + wm0 + l32) * 16
-                                      : ((g >> 1) * BM + wm0 + l16) * 16 + (g & 1) * 8;
-  const uint32_t lane_as = T::kAq + T::kBq + (wm0 + (T::MF == 32 ? 4 * half : 4 * g)) * 4;
-  const uint32_t lane_b = T::MF == 32 ? T::kAq + (half * BN + wn0 + l32) * 16
-                                      : T::kAq + ((g >> 1) * BN + wn0 + l16) * 16 + (g & 1) * 8;
-  const uint32_t lane_bs = T::kAq + T::kBq + T::kAs + (wn0 + (T::MF == 32 ? l32 : l16)) * 8;
+  const uint32_t lane_a = kofs * 2 * BM * 16 +
+                          (T::MF == 32 ? (half * BM + wm0 + l32) * 16
+                                       : ((g >> 1) * BM + wm0 + l16) * 16 + (g & 1) * 8);
+  const uint32_t lane_as =
+      T::kAq + T::kBq + kofs * BM * 4 + (wm0 + (T::MF == 32 ? 4 * half : 4 * g)) * 4;
+  const uint32_t lane_b = T::kAq + kofs * 2 * BN * 16 +
+                          (T::MF == 32 ? (half * BN + wn0 + l32) * 16
+                                       : ((g >> 1) * BN + wn0 + l16) * 16 + (g & 1) * 8);
+  const uint32_t lane_bs =
+      T::kAq + T::kBq + T::kAs + kofs * BN * 8 + (wn0 + (T::MF == 32 ? l32 : l16)) * 8;
   const uint32_t lds_base = lds_addr(smem);
 
   using acc_t = std::conditional_t<T::MF == 32, v16f, v4f>;
@@ -583,8 +601,8 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
     const int kb_next = (s + NBUF - 1) * KBS;
     auto at_block = [&](auto kb_) __attribute__((always_inline)) {
       constexpr int kb = decltype(kb_)::value;
-      issue_quants<T, kb * T::kDmaOps / KBS, (kb + 1) * T::kDmaOps / KBS>(rs, lo, wave, kb_next,
-                                                                           next);
+      issue_quants<T, kb * T::kDmaOps / T::NB, (kb + 1) * T::kDmaOps / T::NB>(rs, lo, wave,
+                                                                             kb_next, next);
     };
     const uint32_t b = lds_base + (s % NBUF) * T::kStage;
     if constexpr (T::MF == 32)
@@ -602,6 +620,34 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
     asm volatile("s_barrier" ::: "memory");
   }
   wait_vmcnt<0>();   // the loads issued past the end are done before LDS is released
+  if constexpr (T::KSPLIT > 1) {
+    // Add the K groups' partial sums, in group order, into group 0's
+    // registers ([slot][lane] floats: conflict-free LDS accesses).
+    constexpr int kSlots = TM * TN * T::kAccN;
+    float* const red = reinterpret_cast<float*>(smem);
+    __syncthreads();   // every wave's loads into LDS have landed, and its reads are done
+    if (kg > 0) {
+      float* const dst = red + ((kg - 1) * T::kWavesT + wt) * kSlots * 64 + lane;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < T::kAccN; ++r) dst[((i * TN + j) * T::kAccN + r) * 64] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int gg = 1; gg < T::KSPLIT; ++gg) {
+      const float* const src = red + ((gg - 1) * T::kWavesT + wt) * kSlots * 64 + lane;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < T::kAccN; ++r) acc[i][j][r] += src[((i * TN + j) * T::kAccN + r) * 64];
+    }
+  }
   {
     // The lane's position again, from the hardware lane count rather than
     // from values kept across the loop, whose registers it needs.
@@ -702,6 +748,9 @@ const TileConfig kTiles[] = {
     {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2, 16>, 4>},   // 2: as 0 on 16x16 MFMAs
     {128, 256, launch_tile<Tile<128, 256, 4, 4, 4, 2>, 4>},       // 3: 16 waves 32x64
     {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2, 32, 1>, 4>},   // 4: as 0, MFMAs first
+    {64, 64, launch_tile<Tile<64, 64, 2, 1, 8, 2, 32, 0, 4>, 4>},     // 5: 4 K groups of 2 waves
+    {64, 128, launch_tile<Tile<64, 128, 2, 2, 8, 2, 32, 0, 2>, 2>},   // 6: 2 K groups of 4 waves (LDS: one per CU)
+    {64, 128, launch_tile<Tile<64, 128, 2, 2, 4, 2, 32, 0, 2>, 4>},   // 7: as 6, stages of 4
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -711,12 +760,20 @@ int pick_tile(int64_t M, int64_t N) {
     const int t = atoi(e);
     if (t >= 0 && t < kNumTiles) return t;
   }
-  // 128x128 tiles with a wave's MFMAs issued ahead of its epilogues, unless
-  // that leaves CUs idle (fewer tiles than the 256 CUs): then 64x128 tiles
-  // double the workgroup count.
-  const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
-  return tiles128 < 256 ? 1 : 4;
-}
+  // Grids of at least two 128x128 tiles per CU: 128x128 tiles with a
+  // wave's MFMAs issued ahead of its epilogues.  Smaller grids would leave
+  // SIMDs with one or two waves, too few to issue the epilogue at rate, so
+  // they take 64x128 or 64x64 tiles whose waves split each stage's blocks
+  // between two or four K groups (more waves for the same outputs):
+  // 64x128 tiles in stages of 4 blocks (two workgroups per CU) when they
+  // are more than one per CU, in stages of 8 (one per CU) when there are at
+  // least 3/4 as many as CUs, else 64x64 tiles in four K groups.
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t t64 = ((M + 63) / 64) * ((N + 127) / 128);
+  if (t128 >= 512) return 4;
+  if (t64 > 256) return 7;
+  if (t64 >= 192) return 6;
+  return 5;}
 
 }  // namespace
 
@@ -728,10 +785,19 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const
 hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a,
                               const uint16_t* d_a, const uint8_t* w_packed, int8_t* q_h,
                               uint16_t* d_h, hipStream_t stream) {
-  // The 32x32-MFMA tiles with 64-column wave tiles (0, 1, 3 and 4) carry the
+  // The 32x32-MFMA tiles with 64-column wave tiles (all but 2) carry the
   // epilogue; the 16x16 variant (2) is replaced by tile 0.
   const int64_t N = 2 * I;
   switch (pick_tile(M, N)) {
+    case 5:
+      return launch_tile_impl<Tile<64, 64, 2, 1, 8, 2, 32, 0, 4>, 4, true>(
+          M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
+    case 6:
+      return launch_tile_impl<Tile<64, 128, 2, 2, 8, 2, 32, 0, 2>, 2, true>(
+          M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
+    case 7:
+      return launch_tile_impl<Tile<64, 128, 2, 2, 4, 2, 32, 0, 2>, 4, true>(
+          M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
     case 1:
       return launch_tile_impl<Tile<64, 128, 2, 2, 2, 2>, 4, true>(M, N, K, q_a, d_a, w_packed,
                                                                   nullptr, N, stream, q_h, d_h);

@@ -164,7 +164,7 @@ def test_gemm_parity_small(orc, M, N, K):
 TILE_SHAPES = [(9, 64, 32), (130, 200, 544), (300, 330, 2080), (257, 520, 1056)]
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7])
 @pytest.mark.parametrize("M,N,K", TILE_SHAPES)
 def test_gemm_parity_every_tile(orc, monkeypatch, tile, M, N, K):
     monkeypatch.setenv("Q8_GEMM_TILE", str(tile))

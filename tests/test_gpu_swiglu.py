@@ -142,3 +142,23 @@ def test_swiglu_gateup_workload(orc, M):
     qg_ = q_h[rows[:, None], (blks[:, None] * 32 + np.arange(32)[None, :])]
     dg_ = d_h[rows, blks][:, None]
     check_swiglu(qg_, dg_, G, absG, U, absU, h_ref, q_ref, d_ref, K, "workload M%d" % M)
+
+
+@pytest.mark.parametrize("tile", [0, 1, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("M,I,K", [(130, 160, 544), (300, 224, 1056)])
+def test_swiglu_every_tile(orc, monkeypatch, tile, M, I, K):
+    """The gated epilogue on every matrix-core tile configuration (forced
+    through its benchmarking switch), including the ones whose waves split
+    K into groups and add their partial sums before the epilogue."""
+    monkeypatch.setenv("Q8_GEMM_TILE", str(tile))
+    qg, dg, qu, du, bg, bu, wp = _gateup(orc, I, K, M)
+    x = workloads.acts_f32(M, K, case=97, tensor=M + tile)
+    qa, da = orc.quantize_rows(x)
+    say("swiglu tile %d M=%d I=%d K=%d" % (tile, M, I, K))
+    qt, dt = qd_to_dev(qa, da)
+    q_h, d_h = q8.q8_gemm_swiglu(qt, dt, wp, I, K)
+    G, absG = orc.gemm(qa, da, qg, dg)
+    U, absU = orc.gemm(qa, da, qu, du)
+    h_ref, q_ref, d_ref = orc.swiglu_quant(G, U)
+    check_swiglu(q_h.cpu().numpy(), d_bits(d_h), G, absG, U, absU, h_ref, q_ref, d_ref, K,
+                 "tile %d M%d I%d K%d" % (tile, M, I, K))
