@@ -39,6 +39,13 @@
 // 16-byte slices in [block][half][row] order, so a fragment load (lane l:
 // row l%32, half l/32) reads 512 contiguous bytes per half-wave.
 //
+// Occupancy.  The epilogue issues at rate only with several waves per SIMD
+// (one wave alone issues an FMA every ~4.6 clocks).  Large grids get them
+// from 128x128 tiles, two workgroups of eight waves per CU, each wave
+// issuing its MFMAs ahead of their epilogues.  Grids with too few tiles for
+// that split every stage's blocks between K groups of waves instead, and
+// add the groups' partial sums through LDS at the end (Tile::KSPLIT).
+//
 // LDS reads are inline asm with immediate offsets: the compiler cannot tell
 // a read of one stage buffer from the asynchronous loads into the other and
 // would wait for those before every read; the buffer a stage reads is
