@@ -20,34 +20,36 @@
 namespace q8 {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;   // K/8 items per row: a whole number of workgroups for K % 1024 == 0
+constexpr int kMaxGridY = 65535;
 
+// Grid: x covers the K/8 items of a row (four per block), y the rows (each
+// y-slice loops over rows y, y + gridDim.y, ... when M exceeds the grid's
+// y limit), so no thread divides by the row length.
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
-    const void* __restrict__ x, int64_t total_threads, int64_t KB, int64_t ldx,
-    int8_t* __restrict__ q, uint16_t* __restrict__ d) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  // Threads past the end still take part in the lane exchange below with
+    const void* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
+    uint16_t* __restrict__ d) {
+  const int t = static_cast<int>(blockIdx.x) * kThreads + static_cast<int>(threadIdx.x);
+  // Items past the row end still take part in the lane exchange below with
   // zeros; they load and store nothing.
-  const bool live = t < total_threads;
-  const int64_t blk = t >> 2;            // block index over [M][KB]
-  const int sub = static_cast<int>(t & 3);
-  const int64_t m = blk / KB;
-  const int64_t kb = blk - m * KB;
-
-  float v[8];
-  if (live) {
-    load8<kBf16>(x, m * ldx + kb * kQK + sub * 8, v);
-  } else {
+  const bool live = t < static_cast<int>(K / 8);
+  const int64_t KB = K / kQK;
+  for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {   // uniform trip count
+    float v[8];
+    if (live) {
+      load8<kBf16>(x, m * ldx + t * 8, v);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-  }
-  uint32_t lo, hi;
-  uint16_t dbits;
-  quantize8(v, lo, hi, dbits);
-  if (live) {
-    *reinterpret_cast<uint2*>(q + blk * kQK + sub * 8) = make_uint2(lo, hi);
-    if (sub == 0) d[blk] = dbits;
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    uint32_t lo, hi;
+    uint16_t dbits;
+    quantize8(v, lo, hi, dbits);
+    if (live) {
+      *reinterpret_cast<uint2*>(q + m * K + t * 8) = make_uint2(lo, hi);
+      if ((t & 3) == 0) d[m * KB + (t >> 2)] = dbits;
+    }
   }
 }
 
@@ -55,15 +57,14 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(
 
 hipError_t launch_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
                            int8_t* q, uint16_t* d, hipStream_t stream) {
-  const int64_t KB = K / kQK;
-  const int64_t total = M * KB * 4;
-  const int64_t grid = (total + kThreads - 1) / kThreads;
+  const dim3 grid(static_cast<uint32_t>((K / 8 + kThreads - 1) / kThreads),
+                  static_cast<uint32_t>(M < kMaxGridY ? M : kMaxGridY));
   if (dtype == 1)
-    hipLaunchKernelGGL(quantize_act_kernel<true>, dim3(static_cast<uint32_t>(grid)),
-                       dim3(kThreads), 0, stream, x, total, KB, ldx, q, d);
+    hipLaunchKernelGGL(quantize_act_kernel<true>, grid, dim3(kThreads), 0, stream, x, M, K, ldx,
+                       q, d);
   else
-    hipLaunchKernelGGL(quantize_act_kernel<false>, dim3(static_cast<uint32_t>(grid)),
-                       dim3(kThreads), 0, stream, x, total, KB, ldx, q, d);
+    hipLaunchKernelGGL(quantize_act_kernel<false>, grid, dim3(kThreads), 0, stream, x, M, K, ldx,
+                       q, d);
   return hipGetLastError();
 }
 
