@@ -384,16 +384,24 @@ template <int MR>
 hipError_t launch_cfg(int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                       const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
   // Q8_GEMV_CFG=<c> (benchmarking aid): c = 0: row slices sized to fill
-  // the CUs, 16 waves x chunks of 4 blocks, nontemporal weight loads
-  // (default); 1: one workgroup per 64-row group, otherwise the same; 2: as
-  // 1 with ordinary loads; 3: as 1 with chunks of 8.
+  // the CUs, 16 waves, nontemporal weight loads, chunks of 8 blocks at M = 1
+  // (all of a wave's blocks at K = 4096), 4 at M = 2..3 and 2 from M = 4 on,
+  // where the activation operands of a chunk take more scalar registers
+  // (measured at N12288 K4096: M1 10.13 vs 10.30 us with chunks of 4, M4
+  // 10.69 vs 10.90, M6 12.0 vs 13.0) (default); 1: one workgroup per 64-row
+  // group, chunks of 4; 2: as 1 with ordinary loads; 3: as 1 with chunks of
+  // 8; 4: row slices with chunks of 4.  The chunk size does not change the
+  // order of any sum.
   int cfg = 0;
   if (const char* e = getenv("Q8_GEMV_CFG")) cfg = atoi(e);
   switch (cfg) {
     case 1: return launch_m<MR, 4, true>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
     case 2: return launch_m<MR, 4, false>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
     case 3: return launch_m<MR, 8, true>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
-    default: return launch_slice<MR, 4>(N, K, q_a, d_a, w_packed, C, ldc, stream);
+    case 4: return launch_slice<MR, 4>(N, K, q_a, d_a, w_packed, C, ldc, stream);
+    default:
+      return launch_slice<MR, MR == 1 ? 8 : (MR <= 3 ? 4 : 2)>(N, K, q_a, d_a, w_packed, C, ldc,
+                                                                stream);
   }
 }
 

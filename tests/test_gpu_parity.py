@@ -175,7 +175,7 @@ def test_gemm_parity_every_tile(orc, monkeypatch, tile, M, N, K):
     check_close(C, C_ref, absdot, K, "tile %d M%d N%d K%d" % (tile, M, N, K))
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("M,N,K", [(1, 70, 96), (3, 200, 1056), (8, 130, 2080), (5, 64, 32)])
 def test_gemv_parity_every_config(orc, monkeypatch, cfg, M, N, K):
     """Every configuration of the decode kernel (forced through its
