@@ -27,6 +27,12 @@
  *     as for any HIP kernel.
  *   - input/output buffers must not overlap.
  *
+ * Environment: Q8_LOG set (and not "0") makes the product calls print their
+ * dispatch decision (decode or matrix-core kernel and its configuration) to
+ * stderr, one line per call.  Q8_GEMM_TILE=<i> and Q8_GEMV_CFG=<c> force a
+ * compiled configuration of the matrix-core or decode kernel (benchmarking
+ * and tests); every configuration computes the same product.
+ *
  * Domain: finite inputs whose block maxima stay below 65504*127 (larger
  * scales overflow binary16).  NaN and infinity are outside the domain.
  */

@@ -2,10 +2,19 @@
 // include/q8.h): host-side argument checks, the one-time device check,
 // dispatch and launch.  No allocation, no synchronisation.
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
 
 #include "q8.h"
+
 #include "q8_kernels.h"
+
+namespace q8 {
+bool log_enabled() {
+  const char* e = getenv("Q8_LOG");
+  return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+}
+}  // namespace q8
 
 namespace {
 

@@ -57,6 +57,7 @@
 // weight tile; when the grid is a multiple of 8 the ids are remapped so
 // each of the 8 XCDs (which receive workgroups round-robin) gets one
 // contiguous range of tiles and keeps its weight tiles in its own L2.
+#include <cstdio>
 #include <cstdlib>
 #include <type_traits>
 #include <utility>
@@ -786,7 +787,12 @@ int pick_tile(int64_t M, int64_t N) {
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                        const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
-  return kTiles[pick_tile(M, N)].launch(M, N, K, q_a, d_a, w_packed, C, ldc, stream);
+  const int t = pick_tile(M, N);
+  if (log_enabled())
+    fprintf(stderr, "q8: product M=%lld N=%lld K=%lld: matrix-core kernel, tile %d (%dx%d)\n",
+            static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K), t,
+            kTiles[t].bm, kTiles[t].bn);
+  return kTiles[t].launch(M, N, K, q_a, d_a, w_packed, C, ldc, stream);
 }
 
 hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a,
@@ -795,7 +801,11 @@ hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a
   // The 32x32-MFMA tiles with 64-column wave tiles (all but 2) carry the
   // epilogue; the 16x16 variant (2) is replaced by tile 0.
   const int64_t N = 2 * I;
-  switch (pick_tile(M, N)) {
+  const int t = pick_tile(M, N);
+  if (log_enabled())
+    fprintf(stderr, "q8: gated step M=%lld I=%lld K=%lld: matrix-core kernel, tile %d\n",
+            static_cast<long long>(M), static_cast<long long>(I), static_cast<long long>(K), t);
+  switch (t) {
     case 5:
       return launch_tile_impl<Tile<64, 64, 2, 1, 8, 2, 32, 0, 4>, 4, true>(
           M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);

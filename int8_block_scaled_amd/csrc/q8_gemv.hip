@@ -25,6 +25,7 @@
 // and is scaled there: acc += float(P) * (d_w * d_a), where the binary16 x
 // binary16 product is exact in binary32.  Waves then add their partial
 // sums in a fixed order through LDS, so results are reproducible.
+#include <cstdio>
 #include <cstdlib>
 
 #include "q8_kernels.h"
@@ -394,6 +395,9 @@ hipError_t launch_cfg(int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d
   // order of any sum.
   int cfg = 0;
   if (const char* e = getenv("Q8_GEMV_CFG")) cfg = atoi(e);
+  if (log_enabled())
+    fprintf(stderr, "q8: product M=%d N=%lld K=%lld: decode kernel, configuration %d\n", MR,
+            static_cast<long long>(N), static_cast<long long>(K), cfg);
   switch (cfg) {
     case 1: return launch_m<MR, 4, true>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
     case 2: return launch_m<MR, 4, false>(N, K, q_a, d_a, w_packed, C, ldc, 16, stream);
@@ -439,6 +443,9 @@ hipError_t launch_gemv_swiglu(int M, int64_t I, int64_t K, const int8_t* q_a,
                               const uint16_t* d_a, const uint8_t* w_packed, int8_t* q_h,
                               uint16_t* d_h, hipStream_t stream) {
   const int64_t N = 2 * I;
+  if (log_enabled())
+    fprintf(stderr, "q8: gated step M=%d I=%lld K=%lld: decode kernel, one workgroup per group\n",
+            M, static_cast<long long>(I), static_cast<long long>(K));
 #define Q8_SWIGLU_M(MR)                                                                     \
   case MR:                                                                                  \
     return launch_m<MR, 4, true, true>(N, K, q_a, d_a, w_packed, nullptr, 0, 16, stream, q_h, \
@@ -461,6 +468,9 @@ hipError_t launch_gemv_act(int M, const void* x, int dtype, int64_t ldx, int64_t
                            const uint8_t* w_packed, float* C, int64_t ldc, int8_t* q_out,
                            uint16_t* d_out, hipStream_t stream) {
   const bool bf16 = dtype == 1;
+  if (log_enabled())
+    fprintf(stderr, "q8: quantise+product M=%d N=%lld K=%lld: fused decode kernel\n", M,
+            static_cast<long long>(N), static_cast<long long>(K));
   switch (M) {
     case 1: return launch_act_m<1>(x, bf16, ldx, N, K, w_packed, C, ldc, q_out, d_out, stream);
     case 2: return launch_act_m<2>(x, bf16, ldx, N, K, w_packed, C, ldc, q_out, d_out, stream);

@@ -64,6 +64,10 @@ hipError_t launch_kv3_decode(const uint8_t* codes, const float* scales, int64_t 
 
 constexpr int kGemvMaxM = 8;       // M <= kGemvMaxM takes the decode kernel
 
+// Q8_LOG set (and not "0") in the environment: the launchers print their
+// dispatch decision (kernel and configuration) to stderr, one line per call.
+bool log_enabled();
+
 inline int64_t num_groups(int64_t N) { return (N + kGroupRows - 1) / kGroupRows; }
 
 // binary16 bits -> binary32 (exact; v_cvt_f32_f16).

@@ -288,3 +288,16 @@ def test_workload_full_size(orc, layer):
         C_ref, absdot = orc.gemm_sampled(qa, da, qw, dw, rows, cols)
         got = C[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)].cpu().numpy()
         check_close(got, C_ref, absdot, K, layer.name)
+
+
+def test_dispatch_log(orc, monkeypatch, capfd):
+    """Q8_LOG names the kernel each product call takes (decode for M <= 8,
+    a matrix-core tile above), on stderr."""
+    monkeypatch.setenv("Q8_LOG", "1")
+    for M, want in ((3, "decode kernel"), (40, "matrix-core kernel, tile")):
+        qa, da, qw, dw = _problem(M, 96, 128, 17 * M)
+        C = _run(qa, da, orc.blocks_from_qd(qw, dw), 96, 128).cpu().numpy()
+        C_ref, absdot = orc.gemm(qa, da, qw, dw)
+        check_close(C, C_ref, absdot, 128, "logged M%d" % M)
+        err = capfd.readouterr().err
+        assert "q8: product M=%d N=96 K=128: %s" % (M, want) in err, err
