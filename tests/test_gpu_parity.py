@@ -206,12 +206,15 @@ def test_gemm_tiny_workload_every_m(orc):
         check_close(C, C_ref[:M], absdot[:M], K, "tiny M=%d" % M)
 
 
-@pytest.mark.parametrize("M", [3, 300])
-def test_gemm_guard_bands(orc, M):
-    """Columns past N (ldc > N) and rows past M are never written."""
+@pytest.mark.parametrize("M,tile", [(3, None), (300, None)] + [(300, t) for t in range(8)])
+def test_gemm_guard_bands(orc, monkeypatch, M, tile):
+    """Columns past N (ldc > N) and rows past M are never written (the
+    default choice, and every matrix-core tile configuration)."""
+    if tile is not None:
+        monkeypatch.setenv("Q8_GEMM_TILE", str(tile))
     N, K, ldc, extra = 70, 160, 96, 5
     qa, da, qw, dw = _problem(M, N, K, 77 + M)
-    say("guard bands M=%d N=%d ldc=%d" % (M, N, ldc))
+    say("guard bands M=%d N=%d ldc=%d tile %s" % (M, N, ldc, tile))
     out = torch.full((M + extra, ldc), float("nan"), dtype=torch.float32, device=DEV)
     view = out[:M]
     C = _run(qa, da, orc.blocks_from_qd(qw, dw), N, K, out=view)
