@@ -271,10 +271,11 @@ def main():
                                             None),
                 "kernel": "gemm_q8_mfma_kernel", "kernel_us": round(mean["gemm_prefill"] * 1e3, 2),
                 "algorithmic_ops_per_launch": ops,
-                # two fp32 FMAs per output and block: 32 per 32-cycle int8 MFMA
-                # tile; two waves of a SIMD together issue one every ~2.7
-                # cycles, so at most 32 / (32 * 2.7) of the MFMA peak
-                "epilogue_ceiling_frac": round(1 / 2.7, 2)}
+                # two fp32 FMAs per output and block: with staging, 36.1 vector
+                # instructions per 32-cycle int8 MFMA (SQ counters); waves of a
+                # SIMD together issue one every ~2.6 cycles at best, so at
+                # most 32 / (36.1 * 2.6) of the MFMA peak at full clock
+                "epilogue_ceiling_frac": round(32 / (36.1 * 2.6), 2)}
 
     sw_us = mean["swiglu_prefill"] * 1e3
     swiglu = {"workload": "M2048 I6144 K4096 (gate+up 12288 x 4096)",
