@@ -59,7 +59,71 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of the benchmark, run device-to-device copies of MIB MiB "
                         "(a kernel of known traffic, to scale hardware byte counters)")
+    p.add_argument("--workloads", action="store_true",
+                   help="instead of the benchmark, time q8_quantize_act and q8_gemm on every "
+                        "workload (tiny, decode, prefill, large up/down, the M512/M509 sweep), "
+                        "one JSON line each")
     return p.parse_args()
+
+
+def workloads_bench(reps=20):
+    """Every workload's product (and its activation quantiser), seeded as in
+    the parity tests: events around each of `reps` launches, median; packed
+    weight copies rotated over at least 512 MB."""
+    import numpy as np
+    import torch
+
+    import int8_block_scaled_amd as q8
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def median_us(call):
+        for i in range(3):
+            call(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for i, (e0, e1) in enumerate(ev):
+            e0.record()
+            call(i)
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+
+    for layer in workloads.ALL_LAYERS:
+        M, N, K = layer.M, layer.N, layer.K
+        w = torch.from_numpy(workloads.weights(layer)).to(dev)
+        qw, dw = q8.q8_quantize_act(w)
+        del w
+        blocks = torch.cat([dw.view(torch.uint8).view(N, K // 32, 2),
+                            qw.view(torch.uint8).view(N, K // 32, 32)], dim=2).contiguous().view(-1)
+        del qw, dw
+        w_bytes = N * (K // 32) * 34
+        copies = max(2, min(8, -(-(512 << 20) // w_bytes)))
+        packs = [q8.q8_pack_weights(blocks, N, K) for _ in range(copies)]
+        del blocks
+        x = workloads.activations(layer)
+        xt = (torch.from_numpy(x).to(dev) if x.dtype == np.float32
+              else torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16))
+        qa, da = q8.q8_quantize_act(xt)
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
+        gemm_us = median_us(lambda i: q8.q8_gemm(qa, da, packs[i % copies], N, K, out=C))
+        quant_us = median_us(lambda i: q8.q8_quantize_act(xt, q=qa, d=da))
+        ops = 2.0 * M * N * K
+        alg = w_bytes + M * (K // 32) * 34 + 4 * M * N
+        tops = ops / (gemm_us * 1e-6) / 1e12
+        gbs = alg / (gemm_us * 1e-6) / 1e9
+        print(json.dumps({"workload": layer.name, "M": M, "N": N, "K": K,
+                          "kernel": "decode" if M <= 8 else "matrix-core",
+                          "gemm_us": round(gemm_us, 2), "tops": round(tops, 1),
+                          "frac_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
+                          "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                          "quantize_us": round(quant_us, 2), "weight_copies": copies,
+                          "timing": "events per launch, median of %d" % reps}), flush=True)
+        del packs, xt, qa, da, C
+        torch.cuda.empty_cache()
 
 
 def copy_calibration(mib):
@@ -94,6 +158,8 @@ def main():
     args = parse()
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
+    if args.workloads:
+        return workloads_bench()
     if args.gpus != 1:
         sys.exit("bench.py measures one GPU: the library has no multi-GPU path "
                  "(the product shards by N or M with no communication). "
