@@ -226,11 +226,15 @@ def test_gemm_guard_bands(orc, monkeypatch, M, tile):
     check_close(host[:M, :N], C_ref, absdot, K, "guarded")
 
 
-@pytest.mark.parametrize("M", [4, 512])
-def test_gemm_deterministic(orc, M):
+@pytest.mark.parametrize("M,tile", [(4, None), (512, None), (512, 4), (512, 5), (512, 7)])
+def test_gemm_deterministic(orc, monkeypatch, M, tile):
+    """Two calls give the same bits (every sum, including the K groups'
+    partial sums, is added in a fixed order)."""
+    if tile is not None:
+        monkeypatch.setenv("Q8_GEMM_TILE", str(tile))
     N, K = 4096, 4096
     qa, da, qw, dw = _problem(M, N, K, 99 + M)
-    say("determinism M=%d N=%d K=%d" % (M, N, K))
+    say("determinism M=%d N=%d K=%d tile %s" % (M, N, K, tile))
     qt, dt = qd_to_dev(qa, da)
     wp = q8.q8_pack_weights(blocks_to_dev(orc.blocks_from_qd(qw, dw)), N, K)
     C1 = q8.q8_gemm(qt, dt, wp, N, K)
