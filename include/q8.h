@@ -31,7 +31,16 @@
  * dispatch decision (decode or matrix-core kernel and its configuration) to
  * stderr, one line per call.  Q8_GEMM_TILE=<i> and Q8_GEMV_CFG=<c> force a
  * compiled configuration of the matrix-core or decode kernel (benchmarking
- * and tests); every configuration computes the same product.
+ * and tests); every configuration computes the same product.  A forced
+ * matrix-core configuration whose 32-bit buffer ranges cannot hold K
+ * (tile rows or columns times K >= 2^32) is ignored.  Q8_GEMM_REMAP=<o>
+ * forces the matrix-core kernel's workgroup order: 0 (tile order), 1 (a
+ * contiguous range of tiles per XCD; only when the tile count is a
+ * multiple of 8), or 2, 4, 8 (the tile grid cut into o x 8/o rectangles,
+ * one per XCD; only when the tile rows divide by o and the tile columns by
+ * 8/o).  Any other value, or one the grid does not admit, is ignored (the
+ * automatic choice is kept).  Values that are not plain decimal numbers
+ * are ignored by all three.
  *
  * Domain: finite inputs whose block maxima stay below 65504*127 (larger
  * scales overflow binary16).  NaN and infinity are outside the domain.

@@ -135,6 +135,31 @@ def _act_dtype(x):
     raise TypeError("x must be float32 or bfloat16")
 
 
+def _qd_out(q, d, M, K, device):
+    """The quantised-row outputs: allocated when absent, else checked to be
+    int8 [M][K] and float16 [M][K/32], contiguous, on the device."""
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=device)
+    if d is None:
+        d = torch.empty((M, K // 32), dtype=torch.float16, device=device)
+    _need_cuda("q", q)
+    _need_cuda("d", d)
+    if q.dtype != torch.int8 or not q.is_contiguous() or tuple(q.shape) != (M, K):
+        raise TypeError("q must be contiguous int8 [M][K]")
+    if d.dtype not in (torch.float16, torch.int16) or not d.is_contiguous() \
+            or tuple(d.shape) != (M, K // 32):
+        raise TypeError("d must be contiguous float16 [M][K/32]")
+    return q, d
+
+
+def _row_length(x, K):
+    """K defaults to the row length; a K beyond it would read past the rows."""
+    K = x.shape[1] if K is None else K
+    if K > x.shape[1]:
+        raise ValueError("K=%d exceeds the row length %d of x" % (K, x.shape[1]))
+    return K
+
+
 def q8_quantize_act(x: torch.Tensor, K: int = None, q: torch.Tensor = None,
                     d: torch.Tensor = None):
     """Rows of x (float32 or bfloat16, [M][ldx], unit column stride) ->
@@ -144,12 +169,9 @@ def q8_quantize_act(x: torch.Tensor, K: int = None, q: torch.Tensor = None,
         raise ValueError("x must be 2-D with unit column stride")
     dt = _act_dtype(x)
     M = x.shape[0]
-    K = x.shape[1] if K is None else K
+    K = _row_length(x, K)
     ldx = x.stride(0) if M > 1 else max(x.stride(0), K)
-    if q is None:
-        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    if d is None:
-        d = torch.empty((M, K // 32), dtype=torch.float16, device=x.device)
+    q, d = _qd_out(q, d, M, K, x.device)
     _check("q8_quantize_act", _load().q8_quantize_act(
         _ptr(x), dt, M, K, ldx, _ptr(q), _ptr(d), _stream(x)))
     return q, d
@@ -191,15 +213,14 @@ def q8_gemm_act(x: torch.Tensor, w_packed: torch.Tensor, N: int, K: int = None,
         raise ValueError("x must be 2-D with unit column stride")
     dt = _act_dtype(x)
     M = x.shape[0]
-    K = x.shape[1] if K is None else K
+    K = _row_length(x, K)
     ldx = x.stride(0) if M > 1 else max(x.stride(0), K)
     if w_packed.numel() < q8_packed_bytes(N, K):
         raise ValueError("w_packed is smaller than the packed layout for N=%d K=%d" % (N, K))
     if (q is None) != (d is None):
         raise ValueError("give both q and d, or neither")
-    if q is None and M > 8:
-        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
-        d = torch.empty((M, K // 32), dtype=torch.float16, device=x.device)
+    if q is not None or M > 8:
+        q, d = _qd_out(q, d, M, K, x.device)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     if out.dtype != torch.float32 or out.dim() != 2 or out.stride(1) != 1 or out.shape[1] < N \
@@ -325,6 +346,8 @@ def q8_attn_pool(x: torch.Tensor, H: int, D: int, out: torch.Tensor = None) -> t
     """Token-major bfloat16 rows x [L][>=H*D] -> pooled block means float32
     [H][ceil(L/64)][D]."""
     ldx = _bf16_rows("x", x)
+    if x.shape[1] < H * D:
+        raise ValueError("x rows hold %d values, fewer than H*D = %d" % (x.shape[1], H * D))
     L = x.shape[0]
     NB = (L + 63) // 64
     if out is None:
@@ -345,11 +368,17 @@ def q8_attn_select(pooled_q: torch.Tensor, pooled_k: torch.Tensor, k: int, kmax:
             raise TypeError("%s must be contiguous float32 [H][NB][D]" % name)
     Hq, NB, D = pooled_q.shape
     Hkv = pooled_k.shape[0]
+    if tuple(pooled_k.shape[1:]) != (NB, D):
+        raise TypeError("pooled_k must be [Hkv][NB][D] with the NB and D of pooled_q")
     kmax = k if kmax is None else kmax
     if idx is None:
         idx = torch.empty((Hkv, NB, kmax), dtype=torch.int32, device=pooled_q.device)
     if cnt is None:
         cnt = torch.empty((Hkv, NB), dtype=torch.int32, device=pooled_q.device)
+    for name, t, shape in (("idx", idx, (Hkv, NB, kmax)), ("cnt", cnt, (Hkv, NB))):
+        _need_cuda(name, t)
+        if t.dtype != torch.int32 or not t.is_contiguous() or tuple(t.shape) != shape:
+            raise TypeError("%s must be contiguous int32 %s" % (name, list(shape)))
     _check("q8_attn_select", _load().q8_attn_select(_ptr(pooled_q), _ptr(pooled_k), Hq, Hkv, NB, D,
                                                     k, kmax, _ptr(idx), _ptr(cnt),
                                                     _stream(pooled_q)))
@@ -368,6 +397,9 @@ def q8_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, Hq: int, Hkv:
         if t.dtype != torch.int32 or not t.is_contiguous():
             raise TypeError("%s must be contiguous int32" % name)
     L = q.shape[0]
+    for name, t, h in (("q", q, Hq), ("k", k, Hkv), ("v", v, Hkv)):
+        if t.shape[0] < L or t.shape[1] < h * D:
+            raise ValueError("%s must hold [L=%d][>=%d] values" % (name, L, h * D))
     NB = (L + 63) // 64
     if idx.dim() != 3 or tuple(idx.shape[:2]) != (Hkv, NB) or tuple(cnt.shape) != (Hkv, NB):
         raise TypeError("idx must be [Hkv][NB][kmax] and cnt [Hkv][NB], NB = ceil(L/64)")

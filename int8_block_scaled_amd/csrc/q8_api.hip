@@ -14,6 +14,15 @@ bool log_enabled() {
   const char* e = getenv("Q8_LOG");
   return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
 }
+
+int env_index(const char* name) {
+  const char* e = getenv(name);
+  if (e == nullptr || *e == '\0') return -1;
+  char* end = nullptr;
+  const long v = strtol(e, &end, 10);
+  if (*end != '\0' || v < 0 || v > 1000) return -1;
+  return static_cast<int>(v);
+}
 }  // namespace q8
 
 namespace {

@@ -63,6 +63,7 @@
 #include <utility>
 
 #include "q8_kernels.h"
+#include "q8_tilemap.h"
 
 namespace q8 {
 namespace {
@@ -508,27 +509,11 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // XCD-aware order: hardware id i lands on XCD i % 8.  remap == 1: each
-  // XCD takes a contiguous range of logical tiles (M-fastest within it).
-  // remap == sm in {2, 4, 8}: the tile grid is cut into sm x (8/sm)
-  // rectangles, one per XCD (M-fastest within it), so that an XCD's
-  // activation rows fit its L2 and are fetched once.
-  int tm, tn;
-  if (remap >= 2) {
-    const int sm = remap, sn = 8 / sm;
-    const int tmx = tiles_m / sm, tnx = static_cast<int>(gridDim.x) / tiles_m / sn;
-    const int x = blockIdx.x & 7, local = blockIdx.x >> 3;
-    tm = (x % sm) * tmx + local % tmx;
-    tn = (x / sm) * tnx + local / tmx;
-  } else {
-    int bid = blockIdx.x;
-    if (remap) {
-      const int per = gridDim.x >> 3;
-      bid = (bid & 7) * per + (bid >> 3);
-    }
-    tm = bid % tiles_m;
-    tn = bid / tiles_m;
-  }
+  // XCD-aware workgroup order (q8_tilemap.h); the launcher passes only an
+  // order the grid admits.
+  const TileCoord tc = tile_of(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), tiles_m,
+                               remap);
+  const int tm = tc.tm, tn = tc.tn;
   const int64_t m0 = static_cast<int64_t>(tm) * BM;
   const int64_t n0 = static_cast<int64_t>(tn) * BN;
   const int64_t g0 = n0 / kGroupRows;
@@ -705,6 +690,20 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   }
 }
 
+// Workgroup order for a tile grid (q8_tilemap.h).  Q8_GEMM_REMAP=<order>
+// overrides the choice only with an order the grid admits; anything else is
+// ignored (and reported under Q8_LOG).
+int workgroup_order(int64_t tiles_m, int64_t tiles_n, int64_t bm, int64_t K) {
+  const int order = choose_order(tiles_m, tiles_n, bm, K);
+  const int forced = env_index("Q8_GEMM_REMAP");
+  if (forced < 0) return order;
+  if (order_admissible(forced, tiles_m, tiles_n)) return forced;
+  if (log_enabled())
+    fprintf(stderr, "q8: Q8_GEMM_REMAP=%d not admissible for a %lldx%lld tile grid; order %d\n",
+            forced, static_cast<long long>(tiles_m), static_cast<long long>(tiles_n), order);
+  return order;
+}
+
 template <class T, int kOcc, bool kSwiglu>
 hipError_t launch_tile_impl(int64_t M, int64_t N, int64_t K, const int8_t* q_a,
                             const uint16_t* d_a, const uint8_t* w_packed, float* C, int64_t ldc,
@@ -715,18 +714,7 @@ hipError_t launch_tile_impl(int64_t M, int64_t N, int64_t K, const int8_t* q_a,
   const int64_t tiles_m = (M + T::BM - 1) / T::BM;
   const int64_t tiles_n = (N + T::BN - 1) / T::BN;
   const int64_t grid = tiles_m * tiles_n;
-  int remap = (grid % 8 == 0) ? 1 : 0;
-  // The activation rows an XCD needs (BM*K bytes per tile row) should stay
-  // in its 4 MB L2: if all tiles_m rows do not fit, split M over sm XCDs.
-  constexpr int64_t kL2Bytes = 4 << 20;
-  if (remap && tiles_m * T::BM * K > kL2Bytes) {
-    for (int sm = 2; sm <= 8; sm *= 2)
-      if (tiles_m % sm == 0 && tiles_n % (8 / sm) == 0 && tiles_m / sm * T::BM * K <= kL2Bytes) {
-        remap = sm;
-        break;
-      }
-  }
-  if (const char* e = getenv("Q8_GEMM_REMAP")) remap = atoi(e);   // benchmarking aid
+  const int remap = workgroup_order(tiles_m, tiles_n, T::BM, K);
   hipLaunchKernelGGL((gemm_q8_mfma_kernel<T, kOcc, kSwiglu>), dim3(static_cast<uint32_t>(grid)),
                      dim3(T::kThreads), 0, stream, q_a, d_a, w_packed, ws, C, M, N, K, KB, NG,
                      ldc, static_cast<int>(tiles_m), remap, q_h, d_h);
@@ -762,12 +750,16 @@ const TileConfig kTiles[] = {
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-int pick_tile(int64_t M, int64_t N) {
-  // Q8_GEMM_TILE=<index> forces a configuration (benchmarking aid).
-  if (const char* e = getenv("Q8_GEMM_TILE")) {
-    const int t = atoi(e);
-    if (t >= 0 && t < kNumTiles) return t;
-  }
+bool tile_fits(int t, int64_t K) { return buffer_ranges_fit(kTiles[t].bm, kTiles[t].bn, K); }
+
+int pick_tile(int64_t M, int64_t N, int64_t K) {
+  // Q8_GEMM_TILE=<index> forces a configuration (benchmarking aid), if it
+  // exists and its buffer ranges hold K.
+  const int forced = env_index("Q8_GEMM_TILE");
+  if (forced >= 0 && forced < kNumTiles && tile_fits(forced, K)) return forced;
+  if (forced >= 0 && log_enabled())
+    fprintf(stderr, "q8: Q8_GEMM_TILE=%d ignored (no such tile, or K=%lld too large for it)\n",
+            forced, static_cast<long long>(K));
   // Grids of at least two 128x128 tiles per CU: 128x128 tiles with a
   // wave's MFMAs issued ahead of its epilogues.  Smaller grids would leave
   // SIMDs with one or two waves, too few to issue the epilogue at rate, so
@@ -787,7 +779,7 @@ int pick_tile(int64_t M, int64_t N) {
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                        const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
-  const int t = pick_tile(M, N);
+  const int t = pick_tile(M, N, K);
   if (log_enabled())
     fprintf(stderr, "q8: product M=%lld N=%lld K=%lld: matrix-core kernel, tile %d (%dx%d)\n",
             static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K), t,
@@ -801,7 +793,7 @@ hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a
   // The 32x32-MFMA tiles with 64-column wave tiles (all but 2) carry the
   // epilogue; the 16x16 variant (2) is replaced by tile 0.
   const int64_t N = 2 * I;
-  const int t = pick_tile(M, N);
+  const int t = pick_tile(M, N, K);
   if (log_enabled())
     fprintf(stderr, "q8: gated step M=%lld I=%lld K=%lld: matrix-core kernel, tile %d\n",
             static_cast<long long>(M), static_cast<long long>(I), static_cast<long long>(K), t);

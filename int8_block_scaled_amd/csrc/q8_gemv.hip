@@ -393,8 +393,8 @@ hipError_t launch_cfg(int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d
   // group, chunks of 4; 2: as 1 with ordinary loads; 3: as 1 with chunks of
   // 8; 4: row slices with chunks of 4.  The chunk size does not change the
   // order of any sum.
-  int cfg = 0;
-  if (const char* e = getenv("Q8_GEMV_CFG")) cfg = atoi(e);
+  const int forced = env_index("Q8_GEMV_CFG");
+  const int cfg = forced > 4 ? 0 : (forced < 0 ? 0 : forced);
   if (log_enabled())
     fprintf(stderr, "q8: product M=%d N=%lld K=%lld: decode kernel, configuration %d\n", MR,
             static_cast<long long>(N), static_cast<long long>(K), cfg);

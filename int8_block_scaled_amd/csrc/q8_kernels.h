@@ -68,6 +68,10 @@ constexpr int kGemvMaxM = 8;       // M <= kGemvMaxM takes the decode kernel
 // dispatch decision (kernel and configuration) to stderr, one line per call.
 bool log_enabled();
 
+// A plain non-negative decimal number from the environment (at most 1000),
+// or -1 when the variable is unset or anything else.
+int env_index(const char* name);
+
 inline int64_t num_groups(int64_t N) { return (N + kGroupRows - 1) / kGroupRows; }
 
 // binary16 bits -> binary32 (exact; v_cvt_f32_f16).

@@ -243,7 +243,8 @@ def test_attn_fwd_validation(L):
     assert call(q=ODD) == ALIGN and call(v=ctypes.c_void_p(0x10008)) == ALIGN
     assert call(ldq=516) == ALIGN
     assert call(dt=0, out=ctypes.c_void_p(0x10008)) == ALIGN        # fp32 out needs 16
-    assert call(dt=1, out=ctypes.c_void_p(0x10008)) not in (NULL, SHAPE, ALIGN, DTYPE)
+    # (a bf16 output at an 8-byte-aligned address passes every argument check:
+    # covered, with no device to launch on, by test_device_error.py)
     assert call(dt=1, ldo=514) == ALIGN
 
 

@@ -162,9 +162,10 @@ def test_gemm_parity_small(orc, M, N, K):
 # choice depends on the shape), forced through its benchmarking switch, on
 # shapes with ragged M, N and K-stage tails.
 TILE_SHAPES = [(9, 64, 32), (130, 200, 544), (300, 330, 2080), (257, 520, 1056)]
+NUM_TILES = 8                # compiled matrix-core tile configurations
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("tile", range(NUM_TILES))
 @pytest.mark.parametrize("M,N,K", TILE_SHAPES)
 def test_gemm_parity_every_tile(orc, monkeypatch, tile, M, N, K):
     monkeypatch.setenv("Q8_GEMM_TILE", str(tile))
@@ -206,7 +207,7 @@ def test_gemm_tiny_workload_every_m(orc):
         check_close(C, C_ref[:M], absdot[:M], K, "tiny M=%d" % M)
 
 
-@pytest.mark.parametrize("M,tile", [(3, None), (300, None)] + [(300, t) for t in range(8)])
+@pytest.mark.parametrize("M,tile", [(3, None), (300, None)] + [(300, t) for t in range(NUM_TILES)])
 def test_gemm_guard_bands(orc, monkeypatch, M, tile):
     """Columns past N (ldc > N) and rows past M are never written (the
     default choice, and every matrix-core tile configuration)."""
