@@ -19,7 +19,8 @@
  *   - all data pointers are DEVICE pointers of the current HIP device;
  *   - work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *     the null stream); calls return at once, never synchronise, never
- *     allocate, and keep no state beyond a one-time per-device check;
+ *     allocate, and keep no state beyond a one-time per-device check (and,
+ *     for q8_gemm_act_noalloc, its per-device workspace address);
  *   - arguments are validated on the host before any HIP call; a failed
  *     check returns its status and enqueues nothing;
  *   - the caller owns every buffer; outputs are overwritten, never read;
@@ -72,7 +73,9 @@ typedef enum q8_status_e Q8_ENUM_BASE {
                            ldx < K, ldc < N, or a grid too large to launch  */
     Q8_ERR_ALIGN = 3,   /* a pointer or a row pitch breaks the stated alignment */
     Q8_ERR_DTYPE = 4,   /* unknown q8_dtype                                  */
-    Q8_ERR_SIZE = 5,    /* *packed_bytes smaller than the packed layout      */
+    Q8_ERR_SIZE = 5,    /* *packed_bytes smaller than the packed layout, or
+                           (q8_gemm_act_noalloc) quantised rows larger than
+                           its static workspace                              */
     Q8_ERR_DEVICE = 6,  /* the current device is not gfx950, or no device    */
     Q8_ERR_LAUNCH = 7   /* the kernel launch was rejected by the runtime     */
 } q8_status;
@@ -186,6 +189,34 @@ q8_status q8_gemm(int64_t M, int64_t N, int64_t K,
 q8_status q8_gemm_act(const void *x, q8_dtype dtype, int64_t M, int64_t N, int64_t K,
                       int64_t ldx, const void *w_packed, float *C, int64_t ldc,
                       int8_t *q_a, uint16_t *d_a, void *stream);
+
+/*
+ * q8_gemm_act_noalloc -- q8_gemm_act for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same operation and the same
+ * kernels, with the quantised rows kept in a workspace the library holds
+ * instead of caller buffers.
+ *
+ * x, dtype, M, N, K, ldx, w_packed, C, ldc, stream  as for q8_gemm_act.
+ *
+ * C is bit-identical to q8_gemm_act's for the same inputs.  For M <= 8 no
+ * workspace is used (one fused kernel).  For M > 8 the rows' codes and
+ * scales, M*K + 2*M*K/32 bytes (the scales at a 256-byte boundary after the
+ * codes), go through a 48 MiB static device array: one per GPU, held by the
+ * library until the process ends, looked up once per device on the first
+ * call that needs it.  Every call on a GPU shares that array, so calls that
+ * may overlap on one GPU (on different streams or from different threads)
+ * race and must be ordered by the caller.  Nothing is allocated, nothing
+ * is synchronised.
+ *
+ * Errors: as q8_gemm_act (no Q8_ERR_NULL for q_a/d_a, which it has not),
+ * plus Q8_ERR_SIZE when M > 8 and the rows exceed the workspace (e.g. M =
+ * 8192 at K = 5120 fits, M = 8192 at K = 17408 does not), and
+ * Q8_ERR_DEVICE if the workspace's address cannot be obtained.
+ */
+q8_status q8_gemm_act_noalloc(const void *x, q8_dtype dtype, int64_t M, int64_t N, int64_t K,
+                              int64_t ldx, const void *w_packed, float *C, int64_t ldc,
+                              void *stream);
 
 /*
  * q8_pack_weights_gateup -- pack the gate and up weights of a gated

@@ -11,6 +11,7 @@ The calls keep the C names:
 * ``q8_quantize_act(x, K=None)``       fp32/bf16 rows -> (int8 q, fp16 d)
 * ``q8_gemm(q_a, d_a, w_packed, N, K)``  C = A W^T in fp32
 * ``q8_gemm_act(x, w_packed, N, K)``  quantise x on the fly, then C = A W^T
+* ``q8_gemm_act_noalloc(x, w_packed, N, K)``  the same with a library-held workspace
 * ``q8_pack_weights_gateup(w_gate, w_up, I, K)``  gate and up weights packed together
 * ``q8_gemm_swiglu(q_a, d_a, w_packed, I, K)``  Q8_0(silu(A Wg^T) * (A Wu^T))
 """
@@ -26,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libq8gemm.so")
 Q8_F32, Q8_BF16 = 0, 1
 STATUS = {0: "Q8_OK", 1: "Q8_ERR_NULL", 2: "Q8_ERR_SHAPE", 3: "Q8_ERR_ALIGN",
           4: "Q8_ERR_DTYPE", 5: "Q8_ERR_SIZE", 6: "Q8_ERR_DEVICE", 7: "Q8_ERR_LAUNCH"}
-EXPORTS = ("q8_pack_weights", "q8_quantize_act", "q8_gemm", "q8_gemm_act",
+EXPORTS = ("q8_pack_weights", "q8_quantize_act", "q8_gemm", "q8_gemm_act", "q8_gemm_act_noalloc",
            "q8_pack_weights_gateup", "q8_gemm_swiglu", "q8_kv3_encode", "q8_kv3_decode",
            "q8_attn_pool", "q8_attn_select", "q8_attn_fwd", "q8_status_string")
 
@@ -58,6 +59,8 @@ def _load():
         L.q8_gemm.restype = ctypes.c_int
         L.q8_gemm_act.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, i64, vp, vp, vp]
         L.q8_gemm_act.restype = ctypes.c_int
+        L.q8_gemm_act_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, i64, vp]
+        L.q8_gemm_act_noalloc.restype = ctypes.c_int
         L.q8_pack_weights_gateup.argtypes = [vp, vp, i64, i64, vp, ctypes.POINTER(sz), vp]
         L.q8_pack_weights_gateup.restype = ctypes.c_int
         L.q8_gemm_swiglu.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
@@ -241,6 +244,32 @@ def q8_packed_bytes_gateup(I: int, K: int) -> int:
     _check("q8_pack_weights_gateup",
            _load().q8_pack_weights_gateup(None, None, I, K, None, ctypes.byref(n), None))
     return n.value
+
+
+def q8_gemm_act_noalloc(x: torch.Tensor, w_packed: torch.Tensor, N: int, K: int = None,
+                        out: torch.Tensor = None) -> torch.Tensor:
+    """As q8_gemm_act, with the quantised rows in the library's static
+    workspace (no device allocation by the library; `out` may be given so
+    that the call allocates nothing at all)."""
+    _need_cuda("x", x)
+    _need_cuda("w_packed", w_packed)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    dt = _act_dtype(x)
+    M = x.shape[0]
+    K = _row_length(x, K)
+    ldx = x.stride(0) if M > 1 else max(x.stride(0), K)
+    if w_packed.numel() < q8_packed_bytes(N, K):
+        raise ValueError("w_packed is smaller than the packed layout for N=%d K=%d" % (N, K))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if out.dtype != torch.float32 or out.dim() != 2 or out.stride(1) != 1 or out.shape[1] < N \
+            or out.shape[0] != M:
+        raise TypeError("out must be float32 [M][>=N] with unit column stride")
+    ldc = out.stride(0) if M > 1 else max(out.stride(0), N)
+    _check("q8_gemm_act_noalloc", _load().q8_gemm_act_noalloc(
+        _ptr(x), dt, M, N, K, ldx, _ptr(w_packed), _ptr(out), ldc, _stream(x)))
+    return out
 
 
 def q8_pack_weights_gateup(w_gate: torch.Tensor, w_up: torch.Tensor, I: int, K: int,

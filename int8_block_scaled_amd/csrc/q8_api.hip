@@ -2,6 +2,7 @@
 // include/q8.h): host-side argument checks, the one-time device check,
 // dispatch and launch.  No allocation, no synchronisation.
 #include <atomic>
+#include <mutex>
 #include <cstdlib>
 #include <cstring>
 
@@ -44,6 +45,43 @@ q8_status check_device() {
   return state == 1 ? Q8_OK : Q8_ERR_DEVICE;
 }
 
+// Workspace of q8_gemm_act_noalloc: the quantised rows (int8 q, then the
+// binary16 scales at a 256-byte boundary) between its two kernels, for
+// callers that cannot allocate.  One copy per GPU, for the life of the
+// process; every call on a GPU uses it, so calls that overlap on one GPU
+// race.  Host code never uses the array's name as an address: each device's
+// copy is looked up once with hipGetSymbolAddress (with that device
+// current) and only that address is passed to kernels.
+constexpr size_t kScratchBytes = size_t(48) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<uint8_t*> g_scratch[kMaxDevices];
+
+// The current device's copy of the workspace, or nullptr if the lookup
+// fails.  Call after check_device().
+uint8_t* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  uint8_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+      return nullptr;
+    p = static_cast<uint8_t*>(addr);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+// Offset of the scales in the workspace after M x K int8 codes.
+size_t scratch_scale_offset(int64_t M, int64_t K) {
+  return (static_cast<size_t>(M * K) + 255) & ~size_t(255);
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Sizes the kernels index with 32-bit grids and 64-bit offsets: keep every
@@ -76,7 +114,7 @@ const char* q8_status_string(q8_status s) {
     case Q8_ERR_SHAPE: return "invalid shape (need K % 32 == 0, K >= 32, N >= 1, M >= 0, ld >= row length)";
     case Q8_ERR_ALIGN: return "misaligned pointer or row pitch";
     case Q8_ERR_DTYPE: return "unknown dtype";
-    case Q8_ERR_SIZE: return "packed buffer too small";
+    case Q8_ERR_SIZE: return "packed buffer too small, or rows too many for the static workspace";
     case Q8_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
     case Q8_ERR_LAUNCH: return "kernel launch failed";
   }
@@ -213,6 +251,40 @@ q8_status q8_gemm_act(const void* x, q8_dtype dtype, int64_t M, int64_t N, int64
     e = q8::launch_gemv_act(static_cast<int>(M), x, static_cast<int>(dtype), ldx, N, K, wp, C,
                             ldc, q_a, d_a, as_stream(stream));
   } else {
+    e = q8::launch_quantize(x, static_cast<int>(dtype), M, K, ldx, q_a, d_a, as_stream(stream));
+    if (e == hipSuccess) e = q8::launch_gemm(M, N, K, q_a, d_a, wp, C, ldc, as_stream(stream));
+  }
+  return e == hipSuccess ? Q8_OK : Q8_ERR_LAUNCH;
+}
+
+q8_status q8_gemm_act_noalloc(const void* x, q8_dtype dtype, int64_t M, int64_t N, int64_t K,
+                              int64_t ldx, const void* w_packed, float* C, int64_t ldc,
+                              void* stream) {
+  if (dtype != Q8_F32 && dtype != Q8_BF16) return Q8_ERR_DTYPE;
+  if (M < 0 || N < 1 || N >= kMaxDim || !valid_k(K) || ldx < K || ldc < N) return Q8_ERR_SHAPE;
+  if (M == 0) return Q8_OK;
+  if (x == nullptr || w_packed == nullptr || C == nullptr) return Q8_ERR_NULL;
+  const int64_t esize = dtype == Q8_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ldx * esize) % 16 != 0 || !aligned(w_packed, 16) || !aligned(C, 4))
+    return Q8_ERR_ALIGN;
+  if (M * (K / q8::kQK) * 4 / 256 >= kMaxDim) return Q8_ERR_SHAPE;
+  if (((M + 127) / 128) * ((N + 127) / 128) >= kMaxDim) return Q8_ERR_SHAPE;
+  // the quantised rows must fit the workspace (decode sizes need none)
+  if (M > q8::kGemvMaxM &&
+      scratch_scale_offset(M, K) + static_cast<size_t>(M * (K / q8::kQK)) * 2 > kScratchBytes)
+    return Q8_ERR_SIZE;
+  const q8_status dev = check_device();
+  if (dev != Q8_OK) return dev;
+  const uint8_t* wp = static_cast<const uint8_t*>(w_packed);
+  hipError_t e;
+  if (M <= q8::kGemvMaxM) {
+    e = q8::launch_gemv_act(static_cast<int>(M), x, static_cast<int>(dtype), ldx, N, K, wp, C,
+                            ldc, nullptr, nullptr, as_stream(stream));
+  } else {
+    uint8_t* ws = scratch_ptr();
+    if (ws == nullptr) return Q8_ERR_DEVICE;
+    int8_t* q_a = reinterpret_cast<int8_t*>(ws);
+    uint16_t* d_a = reinterpret_cast<uint16_t*>(ws + scratch_scale_offset(M, K));
     e = q8::launch_quantize(x, static_cast<int>(dtype), M, K, ldx, q_a, d_a, as_stream(stream));
     if (e == hipSuccess) e = q8::launch_gemm(M, N, K, q_a, d_a, wp, C, ldc, as_stream(stream));
   }
