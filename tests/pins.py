@@ -515,6 +515,38 @@ def pin_kv3_golden(orc):
     assert np.array_equal(out[0], e0) and not np.any(out[2])
 
 
+def pin_kv3_sum_order(orc):
+    """The order of the sum of squares (adjacent pairs, len = 1, 2, 4, ...),
+    fixed by a hand-derived row (D = 64) on which other orders round
+    differently.  y = H x with y_0 = 2^12 (square 2^24), y_1 = 0, y_2 ..
+    y_41 = 1 and the rest 0; x = H y / 64 is exact in binary32 (multiples of
+    1/64 below 2^7) and so is the butterfly back to y.  Adjacent pairs: the
+    level-1 pair (2^24, 0) is exact, every other pair is 0, 1 + 1 = 2 or a
+    sum of such, and each later partial sum with 2^24 in it is 2^24 plus an
+    even number, which binary32 holds exactly (ulp 2 there): S = 2^24 + 40
+    exactly, S/64 = 2^18 + 0.625 exactly, and sqrt of that is 512 +
+    0.000610 = 512 + 10 ulp (ulp 2^-14 at 512; the second-order term is
+    1e-5 ulp): s bits 0x4400000A.  A halving order (len = 32, 16, ...)
+    first adds 2^24 + 1, a tie that rounds to 2^24, and a left-to-right sum
+    loses every one: each gives a different s.  The codes: u_0 = 4096/s
+    lies above the top threshold (code 7); u = 1/s and u = 0 sit at or
+    above the middle threshold 0 (code 4)."""
+    D = 64
+    H = _sylvester(D)
+    y = np.zeros(D, np.int64)
+    y[0] = 4096
+    y[2:42] = 1
+    x = (H @ y).astype(np.float64) / D
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    codes, scales = orc.kv3_encode(x.astype(np.float32)[None, :])
+    assert np.array_equal(orc.fwht(x.astype(np.float32)), y.astype(np.float32))
+    assert scales.view(np.uint32)[0] == 0x4400000A, hex(scales.view(np.uint32)[0])
+    want = [4] * D
+    want[0] = 7
+    w = [sum(want[8 * g + j] << (3 * j) for j in range(8)) for g in range(D // 8)]
+    assert list(codes[0]) == [b for v in w for b in (v & 255, (v >> 8) & 255, v >> 16)]
+
+
 def pin_kv3_code_positions(orc):
     """Code j of a 3-byte group sits at bits 3j..3j+2: decoding rows with a
     single non-middle code at a known position gives back, through the
@@ -717,5 +749,5 @@ ALL_PINS = [pin_f16_roundtrip_all, pin_f16_vs_numpy, pin_quant_golden, pin_quant
             pin_quant_invariants, pin_quant_rows, pin_gemm_golden, pin_gemm_exact,
             pin_gemm_unit_scale, pin_block_dots, pin_gemm_sampled, pin_block_bytes,
             pin_pack_layout, pin_silu, pin_swiglu_golden, pin_swiglu_rows, pin_gateup_layout,
-            pin_kv3_codebook, pin_fwht, pin_kv3_golden, pin_kv3_code_positions, pin_kv3_roundtrip,
+            pin_kv3_codebook, pin_fwht, pin_kv3_golden, pin_kv3_sum_order, pin_kv3_code_positions, pin_kv3_roundtrip,
             pin_attn_dense, pin_attn_masked, pin_attn_invariants, pin_attn_pool, pin_attn_select]

@@ -62,6 +62,10 @@ MUTANTS = {
                              "for (int64_t hq = h * group; hq < h * group + 1; ++hq)"),
     "attn_pool_divisor": ("out[d] = acc / (double)(t1 - t0);", "out[d] = acc / (double)ATTN_BLK;"),
     "attn_diag_block_dropped": ("                take[i] = 1;\n", "                take[i - 1] = 1;\n"),
+    "kv3_sum_sequential": ("for (int len = 1; len < D; len <<= 1)\n            for (int i = 0; i < D; i += 2 * len) v[i] = v[i] + v[i + len];",
+                           "for (int i = 1; i < D; ++i) v[0] = v[0] + v[i];"),
+    "kv3_sum_halving": ("for (int len = 1; len < D; len <<= 1)\n            for (int i = 0; i < D; i += 2 * len) v[i] = v[i] + v[i + len];",
+                        "for (int len = D / 2; len >= 1; len >>= 1)\n            for (int i = 0; i < len; ++i) v[i] = v[i] + v[i + len];"),
     "kv3_sum_not_squared": ("for (int i = 0; i < D; ++i) v[i] = y[i] * y[i];",
                             "for (int i = 0; i < D; ++i) v[i] = y[i];"),
 }
