@@ -261,16 +261,40 @@ FULL_LAYERS = [workloads.DECODE_M1, workloads.DECODE_M4, workloads.PREFILL, work
                workloads.LARGE_DOWN] + workloads.sweep(512) + workloads.sweep(509)
 
 
-def _sample_points(M, N, n, seed):
+# Products up to this size (the prefill workload and every sweep layer) are
+# compared in full; the oracle takes a few seconds on the host's cores.
+FULL_COMPARE_MACS = 2048 * 12288 * 4096
+
+
+def _sample_points(M, N, n, seed, tile=128):
+    """Outputs the oracle recomputes one by one for the largest products:
+    n random outputs; two whole rows and two whole columns; and in every
+    tile x tile output tile its four corners, one point on each of its four
+    edges and one inside (a tile the kernel left unwritten, or wrote from
+    the wrong rows or columns, shows up in all of them)."""
     r = np.random.default_rng(seed)
     rows = [r.integers(0, M, n)]
     cols = [r.integers(0, N, n)]
-    for m in sorted({0, M - 1}):                      # two whole rows (first/last tile)
+    for m in sorted({0, M - 1}):
         rows.append(np.full(N, m))
         cols.append(np.arange(N))
-    for c in sorted({0, N - 1}):                      # two whole columns
+    for c in sorted({0, N - 1}):
         rows.append(np.arange(M))
         cols.append(np.full(M, c))
+    tm, tn = np.meshgrid(np.arange(0, M, tile), np.arange(0, N, tile), indexing="ij")
+    tm, tn = tm.ravel(), tn.ravel()
+    last_m = np.minimum(tm + tile, M) - 1
+    last_n = np.minimum(tn + tile, N) - 1
+
+    def inside(lo, hi):
+        return lo + (r.random(lo.size) * (hi - lo + 1)).astype(np.int64)
+
+    for rr, cc in ((tm, tn), (tm, last_n), (last_m, tn), (last_m, last_n),       # corners
+                   (tm, inside(tn, last_n)), (last_m, inside(tn, last_n)),       # top, bottom
+                   (inside(tm, last_m), tn), (inside(tm, last_m), last_n),       # left, right
+                   (inside(tm, last_m), inside(tn, last_n))):                    # interior
+        rows.append(rr)
+        cols.append(cc)
     return np.concatenate(rows), np.concatenate(cols)
 
 
@@ -284,15 +308,19 @@ def test_workload_full_size(orc, layer):
     say("full size %s: GPU quantise + pack + gemm" % layer.name)
     wp = q8.q8_pack_weights(blocks_to_dev(orc.blocks_from_qd(qw, dw)), N, K)
     qa_t, da_t = q8.q8_quantize_act(x_to_dev(x))
-    C = q8.q8_gemm(qa_t, da_t, wp, N, K)
-    torch.cuda.synchronize()
+    # every output written: the buffer starts as NaN
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    q8.q8_gemm(qa_t, da_t, wp, N, K, out=C)
+    assert bool(torch.isfinite(C).all()), "outputs left unwritten (NaN) or non-finite"
     assert np.array_equal(qa_t.cpu().numpy(), qa), "quantised activations differ"
     assert np.array_equal(d_bits(da_t), da), "activation scales differ"
-    if M * N * K <= 4 * 12288 * 4096:
+    if M * N * K <= FULL_COMPARE_MACS:
+        say("full size %s: oracle, every output" % layer.name)
         C_ref, absdot = orc.gemm(qa, da, qw, dw)
         check_close(C.cpu().numpy(), C_ref, absdot, K, layer.name)
     else:
         rows, cols = _sample_points(M, N, 4096, M + N + K)
+        say("full size %s: oracle, %d sampled outputs (every 128x128 tile)" % (layer.name, rows.size))
         C_ref, absdot = orc.gemm_sampled(qa, da, qw, dw, rows, cols)
         got = C[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)].cpu().numpy()
         check_close(got, C_ref, absdot, K, layer.name)
