@@ -15,7 +15,8 @@ Weights are packed once (not timed).  Packed weight copies are rotated from
 step to step over more than the 256 MB MALL, so weights come from HBM.
 
 value  = prefill throughput, 2*M*N*K / (quantise + GEMM time), in TOPS
-         (int8 multiply-adds counted as 2 ops).
+         (int8 multiply-adds counted as 2 ops); times are the medians over the
+         timed steps of per-launch event pairs.
 roofline = the prefill GEMM kernel alone, timed with HIP events around each
          launch on the stream it runs on, against the 5.0 POP/s dense int8
          matrix-core peak.  "decode" carries the M=1 and M=4 kernels against
@@ -52,7 +53,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--rotate", type=int, default=8, help="packed weight copies cycled over")
+    p.add_argument("--rotate", type=int, default=10,
+                   help="packed weight copies cycled over (at least enough for 512 MB)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -101,7 +103,7 @@ def workloads_bench(reps=20):
                             qw.view(torch.uint8).view(N, K // 32, 32)], dim=2).contiguous().view(-1)
         del qw, dw
         w_bytes = N * (K // 32) * 34
-        copies = max(2, min(8, -(-(512 << 20) // w_bytes)))
+        copies = max(2, min(64, -(-(512 << 20) // w_bytes)))   # >= 512 MB where possible
         packs = [q8.q8_pack_weights(blocks, N, K) for _ in range(copies)]
         del blocks
         x = workloads.activations(layer)
@@ -185,13 +187,15 @@ def main():
                         qw.view(torch.uint8).view(N, K // 32, 32)], dim=2).contiguous().view(-1)
     del qw, dw
     packed0 = q8.q8_pack_weights(blocks, N, K)
-    packs = [packed0] + [packed0.clone() for _ in range(args.rotate - 1)]
+    # enough copies that the rotation spans at least 512 MB (twice the MALL)
+    copies = max(args.rotate, -(-(512 << 20) // packed0.numel()))
+    packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
     # gate/up weight of I = N/2 hidden units: the same rows, read as gate
     # (first half) and up (second half)
     I = N // 2
     bl = blocks.view(N, -1)
     gu0 = q8.q8_pack_weights_gateup(bl[:I].contiguous().view(-1), bl[I:].contiguous().view(-1), I, K)
-    gus = [gu0] + [gu0.clone() for _ in range(args.rotate - 1)]
+    gus = [gu0] + [gu0.clone() for _ in range(copies - 1)]
     del blocks, bl
     xp = torch.from_numpy(workloads.activations(pre).view(np.int16)).to(dev).view(torch.bfloat16)
     x4 = torch.from_numpy(workloads.activations(dec4).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -296,7 +300,9 @@ def main():
 
     dur = {n: np.array([events[i][j][0].elapsed_time(events[i][j][1]) for i in range(args.steps)])
            for j, n in enumerate(names)}                      # ms per launch
-    mean = {n: float(np.mean(v)) for n, v in dur.items()}
+    # medians over the timed steps (p10 / p90 reported beside them)
+    mean = {n: float(np.median(v)) for n, v in dur.items()}
+    pct = {n: (float(np.percentile(v, 10)), float(np.percentile(v, 90))) for n, v in dur.items()}
 
     ops = 2.0 * M * N * K
     t_pre = (mean["quant_prefill"] + mean["gemm_prefill"]) * 1e-3
@@ -332,16 +338,23 @@ def main():
                                                             "q8_gemv.hip", None)}
 
     roofline = {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS,
-                "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                "unit": "TOPS", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                 "traffic": measured_traffic("gemm_prefill_M2048_traffic.json", "q8_gemm.hip",
                                             None),
                 "kernel": "gemm_q8_mfma_kernel", "kernel_us": round(mean["gemm_prefill"] * 1e3, 2),
+                "kernel_us_p10_p90": [round(v * 1e3, 2) for v in pct["gemm_prefill"]],
+                "timing": "median of %d launches, HIP events on the launch stream" % args.steps,
                 "algorithmic_ops_per_launch": ops,
-                # two fp32 FMAs per output and block: with staging, 36.1 vector
-                # instructions per 32-cycle int8 MFMA (SQ counters); waves of a
-                # SIMD together issue one every ~2.6 cycles at best, so at
-                # most 32 / (36.1 * 2.6) of the MFMA peak at full clock
-                "epilogue_ceiling_frac": round(32 / (36.1 * 2.6), 2)}
+                # Two binary32 FMAs per output and block.  Measured on this
+                # chip (probe, 4 waves per SIMD): an int8 MFMA plus 32
+                # independent FMAs take 104 SIMD cycles, because the MFMA and
+                # the vector instructions of its SIMD do not overlap; so at
+                # most 32/104 of the MFMA peak per clock.  The clock is an
+                # assumption: 2.4 GHz in the peak, about 1.9 GHz measured
+                # (GRBM_GUI_ACTIVE over the dispatch) while this kernel runs.
+                "epilogue_ceiling_frac": {"per_clock": round(32 / 104, 3),
+                                          "at_2.4GHz": round(32 / 104, 3),
+                                          "at_1.9GHz": round(32 / 104 * 1.9 / 2.4, 3)}}
 
     sw_us = mean["swiglu_prefill"] * 1e3
     swiglu = {"workload": "M2048 I6144 K4096 (gate+up 12288 x 4096)",
@@ -371,6 +384,8 @@ def main():
                    "weight_copies_rotated": len(packs),
                    "gemm_only_tops": round(gemm_tops, 1),
                    "quantize_prefill_us": round(mean["quant_prefill"] * 1e3, 2),
+                   "quantize_prefill_us_p10_p90": [round(v * 1e3, 2) for v in pct["quant_prefill"]],
+                   "timing": "medians of %d steps (events per launch)" % args.steps,
                    "prefill_pair_us_sustained": round(back["prefill"], 2),
                    "prefill_tops_sustained": round(sustained_tops, 1)},
         "roofline": roofline,
@@ -481,6 +496,17 @@ def attn_bench(q8, workloads, torch, np, dev, reps=10):
             "total_us": round(pool_us + sel_us + fwd_us, 1)}
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(seconds, qa_t, da_t, packs, N, K):
     """The oracle (plain C, OpenMP over rows) on a bounded row sample of the
     prefill product; rows are added until about ``seconds`` of CPU time."""
@@ -509,7 +535,7 @@ def cpu_baseline(seconds, qa_t, da_t, packs, N, K):
         chunk = min(chunk * 2, 64)
     ops = 2.0 * rows * N * K
     return {"value": round(ops / elapsed / 1e12, 6), "unit": "TOPS", "cores": orc.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "prefill product rows 0..%d of 2048 (N12288 K4096), %.1f s" % (rows, elapsed)}
 
 

@@ -690,6 +690,214 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small-M kernel (9 <= M <= 64): the decode kernel's weight stream, with the
+// block dots on the matrix cores.
+//
+// Up to about 64 token rows the product is bound by the weight stream.  The
+// tiled kernel's grid then has few workgroups, each staging operands
+// through LDS a stage at a time, and keeps too little of the stream in
+// flight.  Here, as in the decode kernel, a workgroup owns one packed
+// 64-row group, its 8 waves split K, and each wave loads a chunk of L blocks
+// at once, straight into registers:
+//   - weights: the MFMA's B operand for rows 32j.. of the group is lane l:
+//     row 32j + l%32, half l/32 of the block, i.e. two contiguous 512-byte
+//     runs of the packed pieces: one 16-byte load per lane per 32 rows;
+//   - activations: the A operand, lane l: row 32i + l%32, bytes 16*(l/32) ..
+//     +16 of the block (rows past M read zero through the buffer range);
+//   - scales: the lane's column's d_w (one value per 32-row tile), and the
+//     chunk's d_a, which the wave stages as binary32 in an LDS slot of its
+//     own and reads back with broadcast loads for its accumulator rows.
+// One v_mfma_i32_32x32x32_i8 per 32x32 tile and block, the bias-fold
+// epilogue of the tiled kernel, and the 8 waves' partial sums added in a
+// fixed pairwise tree through LDS.
+// ---------------------------------------------------------------------------
+constexpr int64_t kSmallMaxM = 64;
+
+template <int MT, int L, int W>
+__global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
+    const int8_t* __restrict__ q_a, const uint16_t* __restrict__ d_a,
+    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws, float* __restrict__ C,
+    int64_t M, int64_t N, int64_t K, int64_t KB, int64_t ldc, int kb_per_wave) {
+#if __HIP_DEVICE_COMPILE__
+  // Per-wave LDS slot: the chunk's activation rows [MT*32][L*32 bytes + 16
+  // pad] (the pad spreads a column read over the banks), then its d_a as
+  // binary32 [MT][L][32].  After the loop the space holds the partial sums
+  // of the upper half of the waves ([W/2][MT][2][16][64] floats).
+  constexpr int kRow = L * kQK + 16;
+  constexpr int kAct = MT * 32 * kRow;
+  constexpr int kSlot = kAct + MT * L * 32 * 4;
+  constexpr int kRed = W / 2 * MT * 2 * 16 * 64 * 4;
+  constexpr int kSegs = MT * 32 * 2 * L;          // 16-byte activation pieces per chunk
+  constexpr int kScs = MT * 32 * L;               // activation scales per chunk
+  static_assert(kSegs % 64 == 0 && kScs % 64 == 0, "whole wave loads");
+  __shared__ __align__(16) uint8_t lds[kRed > W * kSlot ? kRed : W * kSlot];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int64_t g = blockIdx.x;
+  const int kb0 = wave * kb_per_wave;
+  const int kb1 = kb0 + kb_per_wave < KB ? kb0 + kb_per_wave : static_cast<int>(KB);
+
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + g * KB * kGroupBlockBytes,
+                                              static_cast<uint32_t>(KB * kGroupBlockBytes));
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(ws + g * KB * kGroupRows,
+                                               static_cast<uint32_t>(KB * kGroupRows * 2));
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(q_a, static_cast<uint32_t>(M * K));
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(d_a, static_cast<uint32_t>(M * KB * 2));
+  const uint32_t ow = static_cast<uint32_t>(half * kPieceBytes + l32 * 16);   // + 512 * j
+  const uint32_t ows = static_cast<uint32_t>(l32 * 2);                        // + 64 * j
+  uint8_t* const slot = lds + wave * kSlot;
+  float* const sslot = reinterpret_cast<float*>(slot + kAct);
+
+  v16f acc[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  v16i bias;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bias[r] = kBiasBits;
+
+  for (int c = kb0; c < kb1; c += L) {
+    v4i wv[L][2], xv[kSegs / 64];
+    uint16_t wsc[L][2], xs[kScs / 64];
+    // Every load of the chunk first.  Weights: blocks past the wave's
+    // range re-read its last block (their terms are dropped below).
+#pragma unroll
+    for (int b = 0; b < L; ++b) {
+      const uint32_t kb = static_cast<uint32_t>(c + b < kb1 ? c + b : kb1 - 1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        wv[b][j] = __builtin_amdgcn_raw_buffer_load_b128(rw, ow + j * 512 + kb * kGroupBlockBytes,
+                                                         0, 0);
+        wsc[b][j] = __builtin_amdgcn_raw_buffer_load_b16(rws, ows + j * 64 + kb * kGroupRows * 2,
+                                                         0, 0);
+      }
+    }
+    // Activations: piece u*64 + lane is row s / (2L), 16 bytes s % (2L) of
+    // the chunk (16 consecutive lanes read 256 contiguous bytes of a row;
+    // rows past M, or bytes past the last block, read zero or are unused).
+#pragma unroll
+    for (int u = 0; u < kSegs / 64; ++u) {
+      const int sg = u * 64 + lane, row = sg / (2 * L), seg = sg % (2 * L);
+      xv[u] = __builtin_amdgcn_raw_buffer_load_b128(
+          ra, static_cast<uint32_t>(row * K + c * kQK + seg * 16), 0, 0);
+    }
+    // Activation scales: item u*64 + lane is row s / L, block s % L.
+#pragma unroll
+    for (int u = 0; u < kScs / 64; ++u) {
+      const int sc = u * 64 + lane, row = sc / L, b = sc % L;
+      xs[u] = __builtin_amdgcn_raw_buffer_load_b16(
+          rsa, c + b < kb1 ? static_cast<uint32_t>((row * KB + c + b) * 2) : kOutOfRange, 0, 0);
+    }
+    // into the slot (this wave's alone; a wave's LDS accesses complete in
+    // order, so no barrier)
+#pragma unroll
+    for (int u = 0; u < kSegs / 64; ++u) {
+      const int sg = u * 64 + lane, row = sg / (2 * L), seg = sg % (2 * L);
+      *reinterpret_cast<v4i*>(slot + row * kRow + seg * 16) = xv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kScs / 64; ++u) {
+      const int sc = u * 64 + lane, row = sc / L, b = sc % L;
+      sslot[((row >> 5) * L + b) * 32 + (row & 31)] = f16_bits_to_f32(xs[u]);
+    }
+#pragma unroll
+    for (int b = 0; b < L; ++b) {
+      const float live = c + b < kb1 ? 1.0f : 0.0f;
+      v2f wp[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float w = f16_bits_to_f32(wsc[b][j]) * live;
+        wp[j] = v2f{w, -kBias * w};
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        // A operand: row 32i + l32, bytes 16*half of block b; d_a of the
+        // lane's rows 8*(r/4) + 4*half + r%4 of tile i
+        const v4i av = *reinterpret_cast<const v4i*>(slot + (32 * i + l32) * kRow + b * kQK +
+                                                     16 * half);
+        v4f da[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          da[q] = *reinterpret_cast<const v4f*>(sslot + (i * L + b) * 32 + 8 * q + 4 * half);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, wv[b][j], bias, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float y = fmaf(__int_as_float(p[r]), wp[j].x, wp[j].y);
+            acc[i][j][r] = fmaf(y, da[r >> 2][r & 3], acc[i][j][r]);
+          }
+        }
+      }
+    }
+  }
+
+  // waves' sums in a fixed tree: wave w + W/2 into w, then w + W/4, ..., 1
+  float* const red = reinterpret_cast<float*>(lds);
+  __syncthreads();   // every wave is done with its slot
+#pragma unroll
+  for (int span = W / 2; span >= 1; span >>= 1) {
+    if (wave >= span && wave < 2 * span) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            red[((((wave - span) * MT + i) * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (wave < span) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[i][j][r] += red[(((wave * MT + i) * 2 + j) * 16 + r) * 64 + lane];
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = g * kGroupRows + 32 * j + l32;
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (m < M) C[m * ldc + n] = acc[i][j][r];
+        }
+    }
+  }
+#endif
+}
+
+template <int MT>
+hipError_t launch_small(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
+                        const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
+  // 8 waves (two per SIMD: up to 190 registers), chunks of 8 blocks for
+  // one 32-row activation tile, 4 for two.  16 waves would cap a wave at
+  // 128 registers, below what the one-tile chunk needs without spilling.
+  constexpr int W = 8;
+  constexpr int L = MT == 1 ? 8 : 4;
+  const int64_t KB = K / kQK;
+  const int64_t NG = num_groups(N);
+  const uint16_t* ws = reinterpret_cast<const uint16_t*>(w_packed + NG * KB * kGroupBlockBytes);
+  const int kb_per_wave = static_cast<int>((KB + W - 1) / W);
+  hipLaunchKernelGGL((gemm_q8_small_kernel<MT, L, W>), dim3(static_cast<uint32_t>(NG)),
+                     dim3(W * 64), 0, stream, q_a, d_a, w_packed, ws, C, M, N, K, KB, ldc,
+                     kb_per_wave);
+  return hipGetLastError();
+}
+
 // Workgroup order for a tile grid (q8_tilemap.h).  Q8_GEMM_REMAP=<order>
 // overrides the choice only with an order the grid admits; anything else is
 // ignored (and reported under Q8_LOG).
@@ -779,6 +987,15 @@ int pick_tile(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                        const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
+  // 9 <= M <= 64: the weight-streaming kernel, unless a tile is forced
+  if (M <= kSmallMaxM && env_index("Q8_GEMM_TILE") < 0) {
+    if (log_enabled())
+      fprintf(stderr, "q8: product M=%lld N=%lld K=%lld: small-M matrix-core kernel, %lld row tiles\n",
+              static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
+              static_cast<long long>((M + 31) / 32));
+    return M <= 32 ? launch_small<1>(M, N, K, q_a, d_a, w_packed, C, ldc, stream)
+                   : launch_small<2>(M, N, K, q_a, d_a, w_packed, C, ldc, stream);
+  }
   const int t = pick_tile(M, N, K);
   if (log_enabled())
     fprintf(stderr, "q8: product M=%lld N=%lld K=%lld: matrix-core kernel, tile %d (%dx%d)\n",

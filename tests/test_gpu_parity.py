@@ -176,6 +176,18 @@ def test_gemm_parity_every_tile(orc, monkeypatch, tile, M, N, K):
     check_close(C, C_ref, absdot, K, "tile %d M%d N%d K%d" % (tile, M, N, K))
 
 
+# The weight-streaming kernel for 9 <= M <= 64 (the default there): every
+# number of 16-row activation tiles, ragged M and N, one block and many.
+@pytest.mark.parametrize("M", [9, 15, 16, 17, 31, 33, 48, 63, 64])
+@pytest.mark.parametrize("N,K", [(70, 96), (200, 1056), (1000, 32), (4100, 4096)])
+def test_small_m_kernel(orc, M, N, K):
+    qa, da, qw, dw = _problem(M, N, K, 3 * M + N + K)
+    say("small-M kernel M=%d N=%d K=%d" % (M, N, K))
+    C = _run(qa, da, orc.blocks_from_qd(qw, dw), N, K).cpu().numpy()
+    C_ref, absdot = orc.gemm(qa, da, qw, dw)
+    check_close(C, C_ref, absdot, K, "small M%d N%d K%d" % (M, N, K))
+
+
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("M,N,K", [(1, 70, 96), (3, 200, 1056), (8, 130, 2080), (5, 64, 32)])
 def test_gemv_parity_every_config(orc, monkeypatch, cfg, M, N, K):
@@ -207,7 +219,8 @@ def test_gemm_tiny_workload_every_m(orc):
         check_close(C, C_ref[:M], absdot[:M], K, "tiny M=%d" % M)
 
 
-@pytest.mark.parametrize("M,tile", [(3, None), (300, None)] + [(300, t) for t in range(NUM_TILES)])
+@pytest.mark.parametrize("M,tile", [(3, None), (40, None), (300, None)] +
+                         [(300, t) for t in range(NUM_TILES)])
 def test_gemm_guard_bands(orc, monkeypatch, M, tile):
     """Columns past N (ldc > N) and rows past M are never written (the
     default choice, and every matrix-core tile configuration)."""
@@ -227,7 +240,7 @@ def test_gemm_guard_bands(orc, monkeypatch, M, tile):
     check_close(host[:M, :N], C_ref, absdot, K, "guarded")
 
 
-@pytest.mark.parametrize("M,tile", [(4, None), (512, None), (512, 4), (512, 5), (512, 7)])
+@pytest.mark.parametrize("M,tile", [(4, None), (40, None), (512, None), (512, 4), (512, 5), (512, 7)])
 def test_gemm_deterministic(orc, monkeypatch, M, tile):
     """Two calls give the same bits (every sum, including the K groups'
     partial sums, is added in a fixed order)."""
@@ -328,9 +341,10 @@ def test_workload_full_size(orc, layer):
 
 def test_dispatch_log(orc, monkeypatch, capfd):
     """Q8_LOG names the kernel each product call takes (decode for M <= 8,
-    a matrix-core tile above), on stderr."""
+    the small-M kernel up to 64, a matrix-core tile above), on stderr."""
     monkeypatch.setenv("Q8_LOG", "1")
-    for M, want in ((3, "decode kernel"), (40, "matrix-core kernel, tile")):
+    for M, want in ((3, "decode kernel"), (40, "small-M matrix-core kernel, 2 row tiles"),
+                    (100, "matrix-core kernel, tile")):
         qa, da, qw, dw = _problem(M, 96, 128, 17 * M)
         C = _run(qa, da, orc.blocks_from_qd(qw, dw), 96, 128).cpu().numpy()
         C_ref, absdot = orc.gemm(qa, da, qw, dw)
