@@ -40,8 +40,12 @@
  * multiple of 8), or 2, 4, 8 (the tile grid cut into o x 8/o rectangles,
  * one per XCD; only when the tile rows divide by o and the tile columns by
  * 8/o).  Any other value, or one the grid does not admit, is ignored (the
- * automatic choice is kept).  Values that are not plain decimal numbers
- * are ignored by all three.
+ * automatic choice is kept).  Q8_GEMM_ACT_FUSED=1 makes q8_gemm_act with
+ * 9 <= M <= 64 run a single kernel that quantises the rows as it streams the
+ * weights (the same codes, scales and C bit for bit; measured slower than
+ * the default two kernels at N12288 K4096, since every workgroup
+ * re-quantises all M rows).  Values that are not plain decimal numbers are
+ * ignored by all four.
  *
  * Domain: finite inputs whose block maxima stay below 65504*127 (larger
  * scales overflow binary16).  NaN and infinity are outside the domain.
@@ -171,7 +175,8 @@ q8_status q8_gemm(int64_t M, int64_t N, int64_t K,
  * quantises the activation blocks it needs as it streams the weights, so
  * the quantised rows never go through memory; C, and q_a/d_a when given,
  * are bit-identical to the two separate calls.  For M > 8 the two kernels
- * run one after the other on the stream, through q_a/d_a.  (The source
+ * run one after the other on the stream, through q_a/d_a (for M <= 64 with
+ * Q8_GEMM_ACT_FUSED=1, one kernel that also writes q_a/d_a; see above).  (The source
  * engine quantises activations on the fly for its int8 GEMM; see the note
  * at the top.)
  *

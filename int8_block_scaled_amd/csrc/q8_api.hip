@@ -250,6 +250,9 @@ q8_status q8_gemm_act(const void* x, q8_dtype dtype, int64_t M, int64_t N, int64
   if (M <= q8::kGemvMaxM) {
     e = q8::launch_gemv_act(static_cast<int>(M), x, static_cast<int>(dtype), ldx, N, K, wp, C,
                             ldc, q_a, d_a, as_stream(stream));
+  } else if (q8::small_act_applies(M, static_cast<int>(dtype), ldx)) {
+    e = q8::launch_small_act(M, x, static_cast<int>(dtype), ldx, N, K, wp, C, ldc, q_a, d_a,
+                             as_stream(stream));
   } else {
     e = q8::launch_quantize(x, static_cast<int>(dtype), M, K, ldx, q_a, d_a, as_stream(stream));
     if (e == hipSuccess) e = q8::launch_gemm(M, N, K, q_a, d_a, wp, C, ldc, as_stream(stream));

@@ -711,14 +711,24 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
 // One v_mfma_i32_32x32x32_i8 per 32x32 tile and block, the bias-fold
 // epilogue of the tiled kernel, and the 8 waves' partial sums added in a
 // fixed pairwise tree through LDS.
+//
+// X selects the activation input: 0, quantised rows q_a/d_a; 1 (binary32)
+// or 2 (bfloat16), unquantised rows x that every wave quantises for its own
+// chunk (quantize8, the code of the quantise kernel, four lanes per block),
+// writing codes and binary32 scales into its slot where the quantised form
+// would have been staged.  Codes and scales are therefore bit-identical to
+// q8_quantize_act's, and C to quantising first; workgroup 0 also stores
+// them to q_out/d_out when those are given.
 // ---------------------------------------------------------------------------
 constexpr int64_t kSmallMaxM = 64;
 
-template <int MT, int L, int W>
+template <int MT, int L, int W, int X>
 __global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
     const int8_t* __restrict__ q_a, const uint16_t* __restrict__ d_a,
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ ws, float* __restrict__ C,
-    int64_t M, int64_t N, int64_t K, int64_t KB, int64_t ldc, int kb_per_wave) {
+    int64_t M, int64_t N, int64_t K, int64_t KB, int64_t ldc, int kb_per_wave,
+    const void* __restrict__ x, int64_t ldx, int8_t* __restrict__ q_out,
+    uint16_t* __restrict__ d_out) {
 #if __HIP_DEVICE_COMPILE__
   // Per-wave LDS slot: the chunk's activation rows [MT*32][L*32 bytes + 16
   // pad] (the pad spreads a column read over the banks), then its d_a as
@@ -743,8 +753,14 @@ __global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
                                               static_cast<uint32_t>(KB * kGroupBlockBytes));
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(ws + g * KB * kGroupRows,
                                                static_cast<uint32_t>(KB * kGroupRows * 2));
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(q_a, static_cast<uint32_t>(M * K));
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(d_a, static_cast<uint32_t>(M * KB * 2));
+  // activation rows: quantised (X == 0) or raw (X != 0; rows past M, and
+  // blocks past the wave's range, read as zero through the range check)
+  constexpr int kEsz = X == 1 ? 4 : 2;
+  const __amdgpu_buffer_rsrc_t ra =
+      X == 0 ? make_rsrc(q_a, static_cast<uint32_t>(M * K))
+             : make_rsrc(x, static_cast<uint32_t>(M * ldx * kEsz));
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(d_a, static_cast<uint32_t>(X == 0 ? M * KB * 2 : 0));
+  const bool store_q = X != 0 && q_out != nullptr && blockIdx.x == 0;
   const uint32_t ow = static_cast<uint32_t>(half * kPieceBytes + l32 * 16);   // + 512 * j
   const uint32_t ows = static_cast<uint32_t>(l32 * 2);                        // + 64 * j
   uint8_t* const slot = lds + wave * kSlot;
@@ -762,10 +778,65 @@ __global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
   for (int r = 0; r < 16; ++r) bias[r] = kBiasBits;
 
   for (int c = kb0; c < kb1; c += L) {
-    v4i wv[L][2], xv[kSegs / 64];
-    uint16_t wsc[L][2], xs[kScs / 64];
-    // Every load of the chunk first.  Weights: blocks past the wave's
-    // range re-read its last block (their terms are dropped below).
+    v4i wv[L][2];
+    uint16_t wsc[L][2];
+    // Raw activations (X != 0): item t = u*64 + lane is row t / (4L), block
+    // (t / 4) % L, values 8*(t % 4) .. +8 of it, so four lanes hold a block
+    // and 4L consecutive lanes a contiguous run of a row.  The first batch of
+    // items is loaded before the weights, the rest after.
+    constexpr int kItems = MT * 32 * L * 4;
+    constexpr int kPB = X == 1 ? 4 : 8;   // items per lane per batch: 32 registers
+    constexpr int kBatches = X == 0 ? 1 : kItems / 64 / kPB;
+    static_assert(X == 0 || kItems % (64 * kPB) == 0, "whole batches");
+    v4i raw[kPB][kEsz / 2];
+    auto load_batch = [&](int bt) {
+#pragma unroll
+      for (int e = 0; e < kPB; ++e) {
+        const int t = (bt * kPB + e) * 64 + lane;
+        const int row = t / (4 * L), b = (t / 4) % L, sub = t % 4;
+        const uint32_t off =
+            c + b < kb1 ? static_cast<uint32_t>((row * ldx + (c + b) * kQK + sub * 8) * kEsz)
+                        : kOutOfRange;
+#pragma unroll
+        for (int h = 0; h < kEsz / 2; ++h)
+          raw[e][h] = __builtin_amdgcn_raw_buffer_load_b128(
+              ra, off == kOutOfRange ? kOutOfRange : off + 16 * h, 0, 0);
+      }
+    };
+    auto quantize_batch = [&](int bt) {
+#pragma unroll
+      for (int e = 0; e < kPB; ++e) {
+        const int t = (bt * kPB + e) * 64 + lane;
+        const int row = t / (4 * L), b = (t / 4) % L, sub = t % 4;
+        float v[8];
+        if constexpr (X == 1) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[4 * h + q] = __int_as_float(raw[e][h][q]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t w = static_cast<uint32_t>(raw[e][0][q]);
+            v[2 * q] = __uint_as_float(w << 16);
+            v[2 * q + 1] = __uint_as_float(w & 0xffff0000u);
+          }
+        }
+        uint32_t lo, hi;
+        uint16_t dbits;
+        quantize8(v, lo, hi, dbits);   // all lanes take part (lane exchanges)
+        *reinterpret_cast<uint2*>(slot + row * kRow + b * kQK + sub * 8) = make_uint2(lo, hi);
+        if (sub == 0) sslot[((row >> 5) * L + b) * 32 + (row & 31)] = f16_bits_to_f32(dbits);
+        if (store_q && row < M && c + b < kb1) {
+          *reinterpret_cast<uint2*>(q_out + row * K + (c + b) * kQK + sub * 8) =
+              make_uint2(lo, hi);
+          if (sub == 0) d_out[row * KB + c + b] = dbits;
+        }
+      }
+    };
+    if constexpr (X != 0) load_batch(0);   // row 0 < M: always live
+    // Weights: blocks past the wave's range re-read its last block (their
+    // terms are dropped below).
 #pragma unroll
     for (int b = 0; b < L; ++b) {
       const uint32_t kb = static_cast<uint32_t>(c + b < kb1 ? c + b : kb1 - 1);
@@ -777,33 +848,48 @@ __global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
                                                          0, 0);
       }
     }
-    // Activations: piece u*64 + lane is row s / (2L), 16 bytes s % (2L) of
-    // the chunk (16 consecutive lanes read 256 contiguous bytes of a row;
-    // rows past M, or bytes past the last block, read zero or are unused).
+    if constexpr (X != 0) {
+      // into the slot (this wave's alone; a wave's LDS accesses complete in
+      // order, so no barrier).  Batches whose rows are all past M are
+      // skipped: those slot rows only feed outputs that are not stored.
+      constexpr int kRowsPerBatch = kPB * 64 / (4 * L);
+#pragma nounroll
+      for (int bt = 0; bt < kBatches && bt * kRowsPerBatch < M; ++bt) {
+        if (bt > 0) load_batch(bt);
+        quantize_batch(bt);
+      }
+    } else {
+      v4i xv[kSegs / 64];
+      uint16_t xs[kScs / 64];
+      // Activations: piece u*64 + lane is row s / (2L), 16 bytes s % (2L)
+      // of the chunk (16 consecutive lanes read 256 contiguous bytes of a
+      // row; rows past M, or bytes past the last block, read zero or are
+      // unused).
 #pragma unroll
-    for (int u = 0; u < kSegs / 64; ++u) {
-      const int sg = u * 64 + lane, row = sg / (2 * L), seg = sg % (2 * L);
-      xv[u] = __builtin_amdgcn_raw_buffer_load_b128(
-          ra, static_cast<uint32_t>(row * K + c * kQK + seg * 16), 0, 0);
-    }
-    // Activation scales: item u*64 + lane is row s / L, block s % L.
+      for (int u = 0; u < kSegs / 64; ++u) {
+        const int sg = u * 64 + lane, row = sg / (2 * L), seg = sg % (2 * L);
+        xv[u] = __builtin_amdgcn_raw_buffer_load_b128(
+            ra, static_cast<uint32_t>(row * K + c * kQK + seg * 16), 0, 0);
+      }
+      // Activation scales: item u*64 + lane is row s / L, block s % L.
 #pragma unroll
-    for (int u = 0; u < kScs / 64; ++u) {
-      const int sc = u * 64 + lane, row = sc / L, b = sc % L;
-      xs[u] = __builtin_amdgcn_raw_buffer_load_b16(
-          rsa, c + b < kb1 ? static_cast<uint32_t>((row * KB + c + b) * 2) : kOutOfRange, 0, 0);
-    }
-    // into the slot (this wave's alone; a wave's LDS accesses complete in
-    // order, so no barrier)
+      for (int u = 0; u < kScs / 64; ++u) {
+        const int sc = u * 64 + lane, row = sc / L, b = sc % L;
+        xs[u] = __builtin_amdgcn_raw_buffer_load_b16(
+            rsa, c + b < kb1 ? static_cast<uint32_t>((row * KB + c + b) * 2) : kOutOfRange, 0,
+            0);
+      }
+      // into the slot (this wave's alone; no barrier)
 #pragma unroll
-    for (int u = 0; u < kSegs / 64; ++u) {
-      const int sg = u * 64 + lane, row = sg / (2 * L), seg = sg % (2 * L);
-      *reinterpret_cast<v4i*>(slot + row * kRow + seg * 16) = xv[u];
-    }
+      for (int u = 0; u < kSegs / 64; ++u) {
+        const int sg = u * 64 + lane, row = sg / (2 * L), seg = sg % (2 * L);
+        *reinterpret_cast<v4i*>(slot + row * kRow + seg * 16) = xv[u];
+      }
 #pragma unroll
-    for (int u = 0; u < kScs / 64; ++u) {
-      const int sc = u * 64 + lane, row = sc / L, b = sc % L;
-      sslot[((row >> 5) * L + b) * 32 + (row & 31)] = f16_bits_to_f32(xs[u]);
+      for (int u = 0; u < kScs / 64; ++u) {
+        const int sc = u * 64 + lane, row = sc / L, b = sc % L;
+        sslot[((row >> 5) * L + b) * 32 + (row & 31)] = f16_bits_to_f32(xs[u]);
+      }
     }
 #pragma unroll
     for (int b = 0; b < L; ++b) {
@@ -880,21 +966,22 @@ __global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
 #endif
 }
 
-template <int MT>
+// 8 waves (two per SIMD: up to 190 registers), chunks of 8 blocks for one
+// 32-row activation tile, 4 for two.  16 waves would cap a wave at 128
+// registers, below what the one-tile chunk needs without spilling.
+template <int MT, int X>
 hipError_t launch_small(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
+                        const void* x, int64_t ldx, int8_t* q_out, uint16_t* d_out,
                         const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
-  // 8 waves (two per SIMD: up to 190 registers), chunks of 8 blocks for
-  // one 32-row activation tile, 4 for two.  16 waves would cap a wave at
-  // 128 registers, below what the one-tile chunk needs without spilling.
   constexpr int W = 8;
   constexpr int L = MT == 1 ? 8 : 4;
   const int64_t KB = K / kQK;
   const int64_t NG = num_groups(N);
   const uint16_t* ws = reinterpret_cast<const uint16_t*>(w_packed + NG * KB * kGroupBlockBytes);
   const int kb_per_wave = static_cast<int>((KB + W - 1) / W);
-  hipLaunchKernelGGL((gemm_q8_small_kernel<MT, L, W>), dim3(static_cast<uint32_t>(NG)),
+  hipLaunchKernelGGL((gemm_q8_small_kernel<MT, L, W, X>), dim3(static_cast<uint32_t>(NG)),
                      dim3(W * 64), 0, stream, q_a, d_a, w_packed, ws, C, M, N, K, KB, ldc,
-                     kb_per_wave);
+                     kb_per_wave, x, ldx, q_out, d_out);
   return hipGetLastError();
 }
 
@@ -993,8 +1080,10 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const
       fprintf(stderr, "q8: product M=%lld N=%lld K=%lld: small-M matrix-core kernel, %lld row tiles\n",
               static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
               static_cast<long long>((M + 31) / 32));
-    return M <= 32 ? launch_small<1>(M, N, K, q_a, d_a, w_packed, C, ldc, stream)
-                   : launch_small<2>(M, N, K, q_a, d_a, w_packed, C, ldc, stream);
+    return M <= 32 ? launch_small<1, 0>(M, N, K, q_a, d_a, nullptr, 0, nullptr, nullptr,
+                                        w_packed, C, ldc, stream)
+                   : launch_small<2, 0>(M, N, K, q_a, d_a, nullptr, 0, nullptr, nullptr,
+                                        w_packed, C, ldc, stream);
   }
   const int t = pick_tile(M, N, K);
   if (log_enabled())
@@ -1002,6 +1091,39 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const
             static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K), t,
             kTiles[t].bm, kTiles[t].bn);
   return kTiles[t].launch(M, N, K, q_a, d_a, w_packed, C, ldc, stream);
+}
+
+// Opt-in (Q8_GEMM_ACT_FUSED=1): at the decode layer's N12288 K4096 every one
+// of the 192 workgroups re-quantises all M rows, and with the quantise loads
+// in the weight stream's critical path the fused kernel measured slower than
+// quantising first (bf16, graph replay: M9 20.9 vs 19.8 us, M32 31.6 vs
+// 21.4, M64 54.0 vs 27.4).
+bool small_act_applies(int64_t M, int dtype, int64_t ldx) {
+  if (M > kSmallMaxM || env_index("Q8_GEMM_TILE") >= 0 || env_index("Q8_GEMM_ACT_FUSED") != 1)
+    return false;
+  // the raw rows' 32-bit buffer range covers every 32-row tile's rows
+  const int64_t rows = (M + 31) / 32 * 32;
+  return rows * ldx * (dtype == 0 ? 4 : 2) < (int64_t(1) << 32);
+}
+
+hipError_t launch_small_act(int64_t M, const void* x, int dtype, int64_t ldx, int64_t N,
+                            int64_t K, const uint8_t* w_packed, float* C, int64_t ldc,
+                            int8_t* q_out, uint16_t* d_out, hipStream_t stream) {
+  if (log_enabled())
+    fprintf(stderr,
+            "q8: product M=%lld N=%lld K=%lld: small-M matrix-core kernel quantising its rows, "
+            "%lld row tiles\n",
+            static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
+            static_cast<long long>((M + 31) / 32));
+  if (dtype == 0)
+    return M <= 32 ? launch_small<1, 1>(M, N, K, nullptr, nullptr, x, ldx, q_out, d_out,
+                                        w_packed, C, ldc, stream)
+                   : launch_small<2, 1>(M, N, K, nullptr, nullptr, x, ldx, q_out, d_out,
+                                        w_packed, C, ldc, stream);
+  return M <= 32 ? launch_small<1, 2>(M, N, K, nullptr, nullptr, x, ldx, q_out, d_out, w_packed,
+                                      C, ldc, stream)
+                 : launch_small<2, 2>(M, N, K, nullptr, nullptr, x, ldx, q_out, d_out, w_packed,
+                                      C, ldc, stream);
 }
 
 hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a,

@@ -44,6 +44,14 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const
 hipError_t launch_gemv_act(int M, const void* x, int dtype, int64_t ldx, int64_t N, int64_t K,
                            const uint8_t* w_packed, float* C, int64_t ldc, int8_t* q_out,
                            uint16_t* d_out, hipStream_t stream);
+// Quantise-and-multiply for kGemvMaxM < M <= 64 in one kernel (the small-M
+// kernel quantising its own chunks), taken only when Q8_GEMM_ACT_FUSED=1;
+// small_act_applies() tells whether a call takes it (otherwise quantise,
+// then multiply).
+bool small_act_applies(int64_t M, int dtype, int64_t ldx);
+hipError_t launch_small_act(int64_t M, const void* x, int dtype, int64_t ldx, int64_t N,
+                            int64_t K, const uint8_t* w_packed, float* C, int64_t ldc,
+                            int8_t* q_out, uint16_t* d_out, hipStream_t stream);
 
 // Block-sparse causal attention (q8_attn.hip); D in {64, 128}, 64-token blocks.
 hipError_t launch_attn_pool(const uint16_t* x, int64_t L, int64_t ldx, int64_t H, int64_t D,

@@ -61,7 +61,58 @@ def test_fused_bitidentical_to_two_calls(orc, dtype, N, K, M):
     check_close(Cn, C_o, absdot, K, "fused %s M%d" % (dtype, M))
 
 
-@pytest.mark.parametrize("M", [9, 130])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N,K", [(70, 96), (200, 1056), (130, 2080)])
+@pytest.mark.parametrize("M", [9, 16, 31, 32, 33, 47, 64])
+def test_fused_small_m_bitidentical_to_two_calls(orc, monkeypatch, dtype, N, K, M):
+    """9 <= M <= 64 with Q8_GEMM_ACT_FUSED=1: the small-M kernel quantises
+    its own chunks; C, q and d are bit-identical to the two calls (ragged N,
+    K not a multiple of a chunk, blocks over the whole binary16 range)."""
+    monkeypatch.setenv("Q8_GEMM_ACT_FUSED", "1")
+    qw, dw, wp = _weights(orc, N, K, 4)
+    x = _as_dtype(_hard_rows(M, K, 300 + M + K), dtype)
+    xt = x_to_dev(x)
+    say("fused small-M vs two calls %s M=%d N=%d K=%d" % (dtype, M, N, K))
+    q_ref, d_ref = q8.q8_quantize_act(xt)
+    C_ref = q8.q8_gemm(q_ref, d_ref, wp, N, K)
+    q = torch.full_like(q_ref, 77)
+    d = torch.full_like(d_ref, 3.0)
+    C = q8.q8_gemm_act(xt, wp, N, K, q=q, d=d)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q_ref), "quantised rows differ"
+    assert np.array_equal(d_bits(d), d_bits(d_ref)), "scales differ"
+    Cn, Cr = C.cpu().numpy(), C_ref.cpu().numpy()
+    assert np.array_equal(Cn.view(np.uint32), Cr.view(np.uint32)), "C differs from the two calls"
+    qa, da = orc.quantize_rows(x)
+    C_o, absdot = orc.gemm(qa, da, qw, dw)
+    check_close(Cn, C_o, absdot, K, "fused small-M %s M%d" % (dtype, M))
+
+
+@pytest.mark.parametrize("M", [9, 33, 64])
+def test_fused_small_m_full_decode_shape(orc, monkeypatch, M):
+    """N12288 K4096 (the decode layer) at small batches, bf16 rows, fused
+    small-M kernel: every output against the two calls, sampled outputs
+    against the oracle."""
+    monkeypatch.setenv("Q8_GEMM_ACT_FUSED", "1")
+    N, K = 12288, 4096
+    qw, dw = orc.quantize_rows(workloads.weights_f32(N, K, case=91, tensor=0))
+    wp = q8.q8_pack_weights(blocks_to_dev(orc.blocks_from_qd(qw, dw)), N, K)
+    x = workloads.f32_to_bf16_bits(_hard_rows(M, K, 500 + M))
+    xt = x_to_dev(x)
+    say("fused small-M full decode shape M=%d" % M)
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    C = q8.q8_gemm_act(xt, wp, N, K, out=out).cpu().numpy()
+    q_ref, d_ref = q8.q8_quantize_act(xt)
+    C2 = q8.q8_gemm(q_ref, d_ref, wp, N, K).cpu().numpy()
+    assert np.array_equal(C.view(np.uint32), C2.view(np.uint32))
+    qa, da = orc.quantize_rows(x)
+    r = np.random.default_rng(5)
+    rows, cols = r.integers(0, M, 512), r.integers(0, N, 512)
+    C_o, absdot = orc.gemm_sampled(qa, da, qw, dw, rows, cols)
+    check_close(C[rows, cols], C_o, absdot, K, "fused small-M full M%d" % M)
+
+
+@pytest.mark.parametrize("M", [65, 130])
 def test_fused_prefill_sizes_use_two_kernels(orc, M):
     N, K = 200, 544
     qw, dw, wp = _weights(orc, N, K, 2)
@@ -94,10 +145,13 @@ def test_fused_decode_workload(orc, layer):
     check_close(C[rows, cols], C_o, absdot, K, "fused %s" % layer.name)
 
 
-def test_fused_row_pitch_and_output_pitch(orc):
+@pytest.mark.parametrize("M,fused", [(3, "0"), (40, "0"), (40, "1")])
+def test_fused_row_pitch_and_output_pitch(orc, monkeypatch, M, fused):
     """x with ldx > K and C with ldc > N: only the first K columns are read,
-    only the first N columns written."""
-    M, N, K, ldx, ldc = 3, 70, 160, 256, 96
+    only the first N columns written (decode kernel, quantise + small-M
+    kernel, and the fused small-M kernel)."""
+    monkeypatch.setenv("Q8_GEMM_ACT_FUSED", fused)
+    N, K, ldx, ldc = 70, 160, 256, 96
     qw, dw, wp = _weights(orc, N, K, 3)
     x = _hard_rows(M, ldx, 55)
     xt = x_to_dev(x)
@@ -108,3 +162,22 @@ def test_fused_row_pitch_and_output_pitch(orc):
     qa, da = orc.quantize_rows(x[:, :K])
     C_o, absdot = orc.gemm(qa, da, qw, dw)
     check_close(host[:, :N], C_o, absdot, K, "pitched")
+
+
+def test_fused_dispatch_log(orc, monkeypatch, capfd):
+    """Q8_LOG: q8_gemm_act takes the fused decode kernel for M <= 8; up to
+    64 the quantiser then the small-M kernel, or with Q8_GEMM_ACT_FUSED=1
+    the small-M kernel quantising its rows; two kernels above."""
+    monkeypatch.setenv("Q8_LOG", "1")
+    N, K = 96, 128
+    qw, dw, wp = _weights(orc, N, K, 6)
+    for M, fused, want in ((3, "1", "fused decode kernel"),
+                           (40, "0", "small-M matrix-core kernel, 2 row tiles"),
+                           (40, "1", "small-M matrix-core kernel quantising its rows"),
+                           (100, "1", "matrix-core kernel, tile")):
+        monkeypatch.setenv("Q8_GEMM_ACT_FUSED", fused)
+        xt = x_to_dev(_hard_rows(M, K, 11 + M))
+        q8.q8_gemm_act(xt, wp, N, K)
+        torch.cuda.synchronize()
+        err = capfd.readouterr().err
+        assert want in err, (M, err)
