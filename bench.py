@@ -118,7 +118,8 @@ def workloads_bench(reps=20):
         tops = ops / (gemm_us * 1e-6) / 1e12
         gbs = alg / (gemm_us * 1e-6) / 1e9
         print(json.dumps({"workload": layer.name, "M": M, "N": N, "K": K,
-                          "kernel": "decode" if M <= 8 else "matrix-core",
+                          "kernel": ("decode" if M <= 8 else
+                                     "small-M matrix-core" if M <= 64 else "matrix-core tiles"),
                           "gemm_us": round(gemm_us, 2), "tops": round(tops, 1),
                           "frac_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
                           "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),

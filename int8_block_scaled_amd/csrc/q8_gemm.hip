@@ -1042,6 +1042,7 @@ const TileConfig kTiles[] = {
     {64, 64, launch_tile<Tile<64, 64, 2, 1, 8, 2, 32, 0, 4>, 4>},     // 5: 4 K groups of 2 waves
     {64, 128, launch_tile<Tile<64, 128, 2, 2, 8, 2, 32, 0, 2>, 2>},   // 6: 2 K groups of 4 waves (LDS: one per CU)
     {64, 128, launch_tile<Tile<64, 128, 2, 2, 4, 2, 32, 0, 2>, 4>},   // 7: as 6, stages of 4
+    {64, 192, launch_tile<Tile<64, 192, 2, 3, 6, 2, 32, 1, 2>, 3>},   // 8: 2 K groups of 6 waves, MFMAs first
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -1060,12 +1061,16 @@ int pick_tile(int64_t M, int64_t N, int64_t K) {
   // SIMDs with one or two waves, too few to issue the epilogue at rate, so
   // they take 64x128 or 64x64 tiles whose waves split each stage's blocks
   // between two or four K groups (more waves for the same outputs):
-  // 64x128 tiles in stages of 4 blocks (two workgroups per CU) when they
-  // are more than one per CU, in stages of 8 (one per CU) when there are at
-  // least 3/4 as many as CUs, else 64x64 tiles in four K groups.
+  // 64x192 tiles of 12 waves (one per CU) when N is whole 192-column tiles
+  // and they make 3/4 to 1 tile per CU; 64x128 tiles in stages of 4 blocks
+  // (two workgroups per CU) when they are more than one per CU, in stages of
+  // 8 (one per CU) when there are at least 3/4 as many as CUs, else 64x64
+  // tiles in four K groups.
   const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
   const int64_t t64 = ((M + 63) / 64) * ((N + 127) / 128);
+  const int64_t t192 = ((M + 63) / 64) * (N / 192);
   if (t128 >= 512) return 4;
+  if (N % 192 == 0 && t192 >= 192 && t192 <= 256) return 8;
   if (t64 > 256) return 7;
   if (t64 >= 192) return 6;
   return 5;}
@@ -1145,6 +1150,9 @@ hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a
           M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
     case 7:
       return launch_tile_impl<Tile<64, 128, 2, 2, 4, 2, 32, 0, 2>, 4, true>(
+          M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
+    case 8:
+      return launch_tile_impl<Tile<64, 192, 2, 3, 6, 2, 32, 1, 2>, 3, true>(
           M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
     case 1:
       return launch_tile_impl<Tile<64, 128, 2, 2, 2, 2>, 4, true>(M, N, K, q_a, d_a, w_packed,

@@ -162,7 +162,7 @@ def test_gemm_parity_small(orc, M, N, K):
 # choice depends on the shape), forced through its benchmarking switch, on
 # shapes with ragged M, N and K-stage tails.
 TILE_SHAPES = [(9, 64, 32), (130, 200, 544), (300, 330, 2080), (257, 520, 1056)]
-NUM_TILES = 8                # compiled matrix-core tile configurations
+NUM_TILES = 9                # compiled matrix-core tile configurations
 
 
 @pytest.mark.parametrize("tile", range(NUM_TILES))
