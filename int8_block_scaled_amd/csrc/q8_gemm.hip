@@ -674,6 +674,32 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   }
   // Output.  32x32: lane holds column wn0 + 32j + l32 and rows
   // 8*(r/4) + 4*half + r%4; 16x16: column wn0 + 16j + l16, rows 4*g + r.
+  // Through a buffer resource over the tile's valid rows when a whole
+  // tile's offsets fit 31 bits: rows past M fall outside the range, and a
+  // lane whose column is past N takes an offset of 2^31 and above, also
+  // outside it, so the stores need no branches and one 32-bit add each.
+  if (int64_t(BM) * ldc * 4 <= (int64_t(1) << 31)) {
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(C + m0 * ldc, static_cast<uint32_t>(rows_valid * ldc * 4));
+    const uint32_t ldc4 = static_cast<uint32_t>(ldc * 4);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t col = n0 + wn0 + T::MF * j + (T::MF == 32 ? l32 : l16);
+      const uint32_t row0 = static_cast<uint32_t>(wm0 + (T::MF == 32 ? 4 * half : 4 * g));
+      const uint32_t lane_off =
+          col < N ? row0 * ldc4 + static_cast<uint32_t>(col) * 4u : 0x80000000u;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < T::kAccN; ++r) {
+          const uint32_t roff =
+              static_cast<uint32_t>(T::MF * i + (T::MF == 32 ? 8 * (r >> 2) + (r & 3) : r)) * ldc4;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, lane_off + roff,
+                                                0, 0);
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int64_t col = n0 + wn0 + T::MF * j + (T::MF == 32 ? l32 : l16);

@@ -240,6 +240,29 @@ def test_gemm_guard_bands(orc, monkeypatch, M, tile):
     check_close(host[:M, :N], C_ref, absdot, K, "guarded")
 
 
+@pytest.mark.parametrize("tile", [None, 4, 8])
+def test_gemm_wide_output_pitch(orc, monkeypatch, tile):
+    """An output pitch so wide that a tile's rows span more than 2^31 bytes
+    (ldc = 2^23 + 64 floats): the matrix-core kernel then stores with
+    per-element checks instead of its buffer range; exactly the M x N
+    outputs are written (2.3 GB output allocation)."""
+    if tile is not None:
+        monkeypatch.setenv("Q8_GEMM_TILE", str(tile))
+    M, N, K, ldc = 70, 200, 64, (1 << 23) + 64
+    qa, da, qw, dw = _problem(M, N, K, 4242)
+    say("wide output pitch M=%d N=%d ldc=%d tile %s" % (M, N, ldc, tile))
+    flat = torch.full(((M - 1) * ldc + N + 64,), float("nan"), dtype=torch.float32, device=DEV)
+    view = flat.as_strided((M, N), (ldc, 1))
+    C = _run(qa, da, orc.blocks_from_qd(qw, dw), N, K, out=view)
+    assert C.data_ptr() == flat.data_ptr()
+    assert int(torch.isfinite(flat).sum()) == M * N, "wrote outside the M x N outputs"
+    host = view.cpu().numpy()
+    del flat, view, C
+    torch.cuda.empty_cache()
+    C_ref, absdot = orc.gemm(qa, da, qw, dw)
+    check_close(host, C_ref, absdot, K, "wide pitch")
+
+
 @pytest.mark.parametrize("M,tile", [(4, None), (40, None), (512, None), (512, 4), (512, 5), (512, 7)])
 def test_gemm_deterministic(orc, monkeypatch, M, tile):
     """Two calls give the same bits (every sum, including the K groups'
