@@ -1069,6 +1069,7 @@ const TileConfig kTiles[] = {
     {64, 128, launch_tile<Tile<64, 128, 2, 2, 8, 2, 32, 0, 2>, 2>},   // 6: 2 K groups of 4 waves (LDS: one per CU)
     {64, 128, launch_tile<Tile<64, 128, 2, 2, 4, 2, 32, 0, 2>, 4>},   // 7: as 6, stages of 4
     {64, 192, launch_tile<Tile<64, 192, 2, 3, 6, 2, 32, 1, 2>, 3>},   // 8: 2 K groups of 6 waves, MFMAs first
+    {128, 384, launch_tile<Tile<128, 384, 4, 3, 3, 2, 32, 0, 1>, 3>},   // 9: 12 waves 32x128, KBS 3
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -1095,6 +1096,12 @@ int pick_tile(int64_t M, int64_t N, int64_t K) {
   const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
   const int64_t t64 = ((M + 63) / 64) * ((N + 127) / 128);
   const int64_t t192 = ((M + 63) / 64) * (N / 192);
+  // 128x384 tiles of 12 waves (one per CU, 32x128 per wave: a quarter fewer
+  // LDS reads per MFMA) when N is whole 384-column tiles and they fill
+  // whole rounds of the 256 CUs; otherwise the last round's idle CUs cost
+  // more than the 3 % they gain.
+  const int64_t t384 = ((M + 127) / 128) * (N / 384);
+  if (N % 384 == 0 && t384 >= 256 && t384 % 256 == 0) return 9;
   if (t128 >= 512) return 4;
   if (N % 192 == 0 && t192 >= 192 && t192 <= 256) return 8;
   if (t64 > 256) return 7;
@@ -1160,10 +1167,12 @@ hipError_t launch_small_act(int64_t M, const void* x, int dtype, int64_t ldx, in
 hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a,
                               const uint16_t* d_a, const uint8_t* w_packed, int8_t* q_h,
                               uint16_t* d_h, hipStream_t stream) {
-  // The 32x32-MFMA tiles with 64-column wave tiles (all but 2) carry the
-  // epilogue; the 16x16 variant (2) is replaced by tile 0.
+  // The 32x32-MFMA tiles with 64-column wave tiles (all but 2 and 9) carry
+  // the epilogue; the 16x16 variant (2) is replaced by tile 0, the
+  // 128-column wave tiles (9) by tile 4.
   const int64_t N = 2 * I;
-  const int t = pick_tile(M, N, K);
+  int t = pick_tile(M, N, K);
+  if (t == 9) t = 4;   // 128-column wave tiles cannot pair gate and up columns
   if (log_enabled())
     fprintf(stderr, "q8: gated step M=%lld I=%lld K=%lld: matrix-core kernel, tile %d\n",
             static_cast<long long>(M), static_cast<long long>(I), static_cast<long long>(K), t);

@@ -162,7 +162,7 @@ def test_gemm_parity_small(orc, M, N, K):
 # choice depends on the shape), forced through its benchmarking switch, on
 # shapes with ragged M, N and K-stage tails.
 TILE_SHAPES = [(9, 64, 32), (130, 200, 544), (300, 330, 2080), (257, 520, 1056)]
-NUM_TILES = 9                # compiled matrix-core tile configurations
+NUM_TILES = 10               # compiled matrix-core tile configurations
 
 
 @pytest.mark.parametrize("tile", range(NUM_TILES))
@@ -263,7 +263,7 @@ def test_gemm_wide_output_pitch(orc, monkeypatch, tile):
     check_close(host, C_ref, absdot, K, "wide pitch")
 
 
-@pytest.mark.parametrize("M,tile", [(4, None), (40, None), (512, None), (512, 4), (512, 5), (512, 7)])
+@pytest.mark.parametrize("M,tile", [(4, None), (40, None), (512, None), (512, 4), (512, 5), (512, 7), (512, 9)])
 def test_gemm_deterministic(orc, monkeypatch, M, tile):
     """Two calls give the same bits (every sum, including the K groups'
     partial sums, is added in a fixed order)."""

@@ -144,7 +144,7 @@ def test_swiglu_gateup_workload(orc, M):
     check_swiglu(qg_, dg_, G, absG, U, absU, h_ref, q_ref, d_ref, K, "workload M%d" % M)
 
 
-@pytest.mark.parametrize("tile", [0, 1, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("tile", [0, 1, 3, 4, 5, 6, 7, 8, 9])
 @pytest.mark.parametrize("M,I,K", [(130, 160, 544), (300, 224, 1056)])
 def test_swiglu_every_tile(orc, monkeypatch, tile, M, I, K):
     """The gated epilogue on every matrix-core tile configuration (forced
