@@ -649,13 +649,16 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
     const int half = lane_o >> 5, l32 = lane_o & 31, g = lane_o >> 4, l16 = lane_o & 15;
 
   if constexpr (kSwiglu) {
-    // The wave's 64 columns are one row group: column l32 is the gate of
-    // hidden unit 32*grp + l32 and column 32 + l32 its up, both in this lane
-    // (j = 0 and 1); a half-wave's 32 lanes hold one 32-unit block of a row.
-    static_assert(T::MF == 32 && T::TN == 2, "one 64-column row group per wave");
-    const int64_t grp = (n0 + wn0) / kGroupRows;
-    if (n0 + wn0 < N) {
-      const int64_t I = N / 2;
+    // Each 64 columns of the wave are one row group: column 64p + l32 is the
+    // gate of hidden unit 32*grp + l32 and column 64p + 32 + l32 its up, both
+    // in this lane (j = 2p and 2p + 1); a half-wave's 32 lanes hold one
+    // 32-unit block of a row.
+    static_assert(T::MF == 32 && T::TN % 2 == 0, "whole 64-column row groups per wave");
+    const int64_t I = N / 2;
+#pragma unroll
+    for (int pr = 0; pr < TN / 2; ++pr) {
+      const int64_t grp = (n0 + wn0) / kGroupRows + pr;
+      if (grp * kGroupRows >= N) continue;
       const int64_t hid = grp * 32 + l32;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -663,7 +666,8 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
         for (int r = 0; r < 16; ++r) {
           const int64_t row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
           uint16_t dbits;
-          const int q = quantize_lane32(silu_mul(acc[i][0][r], acc[i][1][r]), dbits);
+          const int q =
+              quantize_lane32(silu_mul(acc[i][2 * pr][r], acc[i][2 * pr + 1][r]), dbits);
           if (row < M) {
             q_h[row * I + hid] = static_cast<int8_t>(q);
             if (l32 == 0) d_h[row * (I / kQK) + grp] = dbits;
@@ -1167,12 +1171,11 @@ hipError_t launch_small_act(int64_t M, const void* x, int dtype, int64_t ldx, in
 hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a,
                               const uint16_t* d_a, const uint8_t* w_packed, int8_t* q_h,
                               uint16_t* d_h, hipStream_t stream) {
-  // The 32x32-MFMA tiles with 64-column wave tiles (all but 2 and 9) carry
-  // the epilogue; the 16x16 variant (2) is replaced by tile 0, the
-  // 128-column wave tiles (9) by tile 4.
+  // The 32x32-MFMA tiles (all but 2) carry the epilogue: their wave tiles
+  // are whole 64-column row groups; the 16x16 variant (2) is replaced by
+  // tile 0.
   const int64_t N = 2 * I;
-  int t = pick_tile(M, N, K);
-  if (t == 9) t = 4;   // 128-column wave tiles cannot pair gate and up columns
+  const int t = pick_tile(M, N, K);
   if (log_enabled())
     fprintf(stderr, "q8: gated step M=%lld I=%lld K=%lld: matrix-core kernel, tile %d\n",
             static_cast<long long>(M), static_cast<long long>(I), static_cast<long long>(K), t);
@@ -1185,6 +1188,9 @@ hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a
           M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
     case 7:
       return launch_tile_impl<Tile<64, 128, 2, 2, 4, 2, 32, 0, 2>, 4, true>(
+          M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
+    case 9:
+      return launch_tile_impl<Tile<128, 384, 4, 3, 3, 2, 32, 0, 1>, 3, true>(
           M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
     case 8:
       return launch_tile_impl<Tile<64, 192, 2, 3, 6, 2, 32, 1, 2>, 3, true>(
