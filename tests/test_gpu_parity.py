@@ -144,6 +144,47 @@ def test_gemm_unit_scale_is_exact_integer(orc, M, K):
     assert np.array_equal(C.astype(np.float64), want)
 
 
+NUM_TILES = 10               # compiled matrix-core tile configurations
+
+
+def _index_problem(M, N, K, which):
+    """Index-encoded operands with unit scales: one side one-hot (row m
+    selects k = m % K), the other a code of its (row, k) position, so every
+    output is one known code and a misplaced operand or result lane (a
+    transposed fragment, a swapped half, a wrong row or column of a tile)
+    changes it."""
+    m = np.arange(M)[:, None]
+    n = np.arange(N)[:, None]
+    k = np.arange(K)[None, :]
+    if which == "a_onehot":
+        qa = (k == m % K).astype(np.int8)
+        qw = ((n * 7 + k * 3) % 251 - 125).astype(np.int8)
+    else:
+        qa = ((m * 5 + k * 11) % 251 - 125).astype(np.int8)
+        qw = (k == n % K).astype(np.int8)
+    one = lambda rows: np.full((rows, K // 32), 0x3C00, np.uint16)
+    return qa, one(M), qw, one(N)
+
+
+INDEX_CASES = [(1, 200, 64, None), (5, 200, 96, None), (8, 4100, 64, None), (9, 200, 64, None),
+               (40, 4100, 96, None), (64, 200, 64, None), (130, 200, 96, None),
+               (300, 1000, 64, None)]
+
+
+@pytest.mark.parametrize("which", ["a_onehot", "w_onehot"])
+@pytest.mark.parametrize("M,N,K,tile", INDEX_CASES + [(300, 1000, 96, t) for t in range(NUM_TILES)])
+def test_gemm_lane_layout_index_encoded(orc, monkeypatch, which, M, N, K, tile):
+    """Operand and result lane mappings of every kernel (decode, small-M,
+    each matrix-core tile), checked exactly with index-encoded inputs."""
+    if tile is not None:
+        monkeypatch.setenv("Q8_GEMM_TILE", str(tile))
+    qa, da, qw, dw = _index_problem(M, N, K, which)
+    say("index-encoded %s M=%d N=%d K=%d tile %s" % (which, M, N, K, tile))
+    C = _run(qa, da, orc.blocks_from_qd(qw, dw), N, K).cpu().numpy()
+    want = (qa.astype(np.int64) @ qw.astype(np.int64).T).astype(np.float64)
+    assert np.array_equal(C.astype(np.float64), want)
+
+
 SMALL_SHAPES = [(M, 256, 512) for M in range(1, 10)] + [
     (16, 256, 512), (17, 70, 96), (33, 130, 160), (127, 200, 544), (128, 128, 128),
     (129, 64, 32), (255, 257, 1056), (300, 330, 2080), (509, 640, 1024)]
@@ -162,7 +203,6 @@ def test_gemm_parity_small(orc, M, N, K):
 # choice depends on the shape), forced through its benchmarking switch, on
 # shapes with ragged M, N and K-stage tails.
 TILE_SHAPES = [(9, 64, 32), (130, 200, 544), (300, 330, 2080), (257, 520, 1056)]
-NUM_TILES = 10               # compiled matrix-core tile configurations
 
 
 @pytest.mark.parametrize("tile", range(NUM_TILES))
