@@ -71,6 +71,27 @@ def test_kv3_encode_pitch(orc, D, dtype):
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("R", [1, 7, 1001])
+def test_kv3_encode_guard_bands(orc, D, R):
+    """Codes and scales are written exactly where the rows go: sentinel rows
+    before and after each output stay intact."""
+    x_np = _inputs(R, D, "bf16", 11 + R)
+    say("kv3 encode guard bands R=%d D=%d" % (R, D))
+    row, pad = 3 * D // 8, 64                    # pad keeps the outputs 16-byte aligned
+    cbuf = torch.full((pad + R * row + pad,), 0xA5, dtype=torch.uint8, device=DEV)
+    sbuf = torch.full((16 + R + 16,), -7.0, dtype=torch.float32, device=DEV)
+    q8.q8_kv3_encode(x_to_dev(x_np), codes=cbuf[pad:pad + R * row].view(R, row),
+                     scales=sbuf[16:16 + R])
+    c, s = cbuf.cpu().numpy(), sbuf.cpu().numpy()
+    assert np.all(c[:pad] == 0xA5) and np.all(c[pad + R * row:] == 0xA5), \
+        "codes written outside their rows"
+    assert np.all(s[:16] == -7.0) and np.all(s[16 + R:] == -7.0), "scales written outside their rows"
+    c_ref, s_ref = orc.kv3_encode(x_np, D)
+    assert np.array_equal(c[pad:pad + R * row].reshape(R, row), c_ref)
+    assert np.array_equal(_bits(s[16:16 + R]), _bits(s_ref))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("R", [1, 5, 1001])
 def test_kv3_decode_bitexact(orc, D, R):
     """Decode the oracle's codes (so the input does not come from the kernel

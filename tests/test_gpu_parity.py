@@ -67,6 +67,24 @@ def test_quantize_row_pitch(orc):
     assert np.array_equal(q.cpu().numpy(), qr) and np.array_equal(d_bits(d), dr)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,K", [(1, 32), (5, 96), (9, 1056), (300, 2080)])
+def test_quantize_guard_bands(orc, dtype, M, K):
+    """q and d are written exactly where the rows go: a row of sentinels
+    before and after each output (and the bytes around them) stays intact."""
+    x = _random_scale_rows(M, K, 31 + M)
+    xs = x if dtype == "f32" else workloads.f32_to_bf16_bits(x)
+    say("quantize guard bands %s M=%d K=%d" % (dtype, M, K))
+    qbuf = torch.full((M + 2, K), 77, dtype=torch.int8, device=DEV)
+    dbuf = torch.full((M + 2, K // 32), 3.0, dtype=torch.float16, device=DEV)
+    q8.q8_quantize_act(x_to_dev(xs), q=qbuf[1:M + 1], d=dbuf[1:M + 1])
+    qh, dh = qbuf.cpu().numpy(), d_bits(dbuf)
+    assert np.all(qh[0] == 77) and np.all(qh[M + 1] == 77), "q written outside its rows"
+    assert np.all(dh[0] == 0x4200) and np.all(dh[M + 1] == 0x4200), "d written outside its rows"
+    qr, dr = orc.quantize_rows(xs)
+    assert np.array_equal(qh[1:M + 1], qr) and np.array_equal(dh[1:M + 1], dr)
+
+
 QUANT_LAYERS = [workloads.TINY, workloads.DECODE_M4, workloads.PREFILL, workloads.LARGE_UP,
                 workloads.LARGE_DOWN] + workloads.sweep(509)[::3]
 

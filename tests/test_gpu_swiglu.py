@@ -162,3 +162,25 @@ def test_swiglu_every_tile(orc, monkeypatch, tile, M, I, K):
     h_ref, q_ref, d_ref = orc.swiglu_quant(G, U)
     check_swiglu(q_h.cpu().numpy(), d_bits(d_h), G, absG, U, absU, h_ref, q_ref, d_ref, K,
                  "tile %d M%d I%d K%d" % (tile, M, I, K))
+
+
+@pytest.mark.parametrize("M", [3, 40, 300])
+def test_swiglu_guard_bands(orc, M):
+    """q_h and d_h are written exactly where the rows go (decode kernel,
+    small M, matrix-core tiles): sentinel rows before and after stay intact,
+    and the rows between match a call into fresh buffers bit for bit."""
+    I, K = 160, 544
+    qg, dg, qu, du, bg, bu, wp = _gateup(orc, I, K, 90 + M)
+    x = workloads.acts_f32(M, K, case=98, tensor=M)
+    qa, da = orc.quantize_rows(x)
+    qt, dt = qd_to_dev(qa, da)
+    say("swiglu guard bands M=%d I=%d K=%d" % (M, I, K))
+    qbuf = torch.full((M + 2, I), 77, dtype=torch.int8, device=DEV)
+    dbuf = torch.full((M + 2, I // 32), 3.0, dtype=torch.float16, device=DEV)
+    q8.q8_gemm_swiglu(qt, dt, wp, I, K, q=qbuf[1:M + 1], d=dbuf[1:M + 1])
+    q_ref, d_ref = q8.q8_gemm_swiglu(qt, dt, wp, I, K)
+    qh, dh = qbuf.cpu().numpy(), d_bits(dbuf)
+    assert np.all(qh[0] == 77) and np.all(qh[M + 1] == 77), "q_h written outside its rows"
+    assert np.all(dh[0] == 0x4200) and np.all(dh[M + 1] == 0x4200), "d_h written outside its rows"
+    assert np.array_equal(qh[1:M + 1], q_ref.cpu().numpy())
+    assert np.array_equal(dh[1:M + 1], d_bits(d_ref))
