@@ -25,9 +25,12 @@
 // is exact: d_w has 11 significant bits).  Against 1024 int8 MACs per clock
 // per SIMD, 32 unpacked binary32 FMAs per 32-cycle MFMA tile cap the kernel
 // well below the matrix-core peak: a single wave issues an FMA every ~4.6
-// clocks, two waves of a SIMD together one every ~2.7 (measured), so the cap
-// lies between 1/4 and ~3/8 of the peak, and the kernel is built to keep the
-// VALU issuing epilogue FMAs and little else.
+// clocks, two waves of a SIMD together one every ~2.2-2.7 (measured), and
+// an MFMA blocks vector issue on its SIMD while it executes, so one MFMA and
+// its 32 FMAs take at least ~104 SIMD cycles: about 0.3 of the peak per
+// clock.  The kernel is built to keep the VALU issuing epilogue FMAs and
+// little else, and to move as little data as it can: it runs at the chip's
+// power limit, where saved data movement comes back as clock.
 //
 // Data movement.  A workgroup of WAVES_M x WAVES_N waves owns a BM x BN
 // output tile; K advances in stages of KBS blocks through two LDS buffers.
@@ -41,10 +44,13 @@
 //
 // Occupancy.  The epilogue issues at rate only with several waves per SIMD
 // (one wave alone issues an FMA every ~4.6 clocks).  Large grids get them
-// from 128x128 tiles, two workgroups of eight waves per CU, each wave
-// issuing its MFMAs ahead of their epilogues.  Grids with too few tiles for
-// that split every stage's blocks between K groups of waves instead, and
-// add the groups' partial sums through LDS at the end (Tile::KSPLIT).
+// from 128x384 tiles of twelve 32x128 waves (one workgroup per CU, three
+// waves per SIMD; a 32x128 wave tile reads its activation scales once for
+// four MFMAs) when N and the grid suit them, else from 128x128 tiles, two
+// workgroups of eight waves per CU, each wave issuing its MFMAs ahead of
+// their epilogues.  Grids with too few tiles split every stage's blocks
+// between K groups of waves instead, and add the groups' partial sums
+// through LDS at the end (Tile::KSPLIT).
 //
 // LDS reads are inline asm with immediate offsets: the compiler cannot tell
 // a read of one stage buffer from the asynchronous loads into the other and
@@ -53,10 +59,11 @@
 // loads before it).  The reads' completion is awaited explicitly before
 // their values are used, and the asm carries a memory clobber.
 //
-// Workgroup order: tiles run M-fastest so consecutive workgroups share a
-// weight tile; when the grid is a multiple of 8 the ids are remapped so
-// each of the 8 XCDs (which receive workgroups round-robin) gets one
-// contiguous range of tiles and keeps its weight tiles in its own L2.
+// Workgroup order (q8_tilemap.h): tiles run M-fastest so consecutive
+// workgroups share a weight tile; when the grid is a multiple of 8 the ids
+// are remapped so each of the 8 XCDs (which receive workgroups round-robin)
+// gets one contiguous range, or one rectangle, of tiles and keeps its
+// operand panels in its own L2.
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
