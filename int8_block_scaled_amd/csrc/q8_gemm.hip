@@ -1068,21 +1068,39 @@ struct TileConfig {
   launcher_t launch;
 };
 
-// Compiled tile configurations.  Occupancy hint = waves per SIMD the
-// register allocation must allow.
+// Compiled tile configurations (index = the one in q8_tilemap.h's
+// kTileDims).  Occupancy hint = waves per SIMD the register allocation must
+// allow.
+using Tile0 = Tile<128, 128, 4, 2, 4, 2>;                    // 8 waves 32x64, KBS 4
+using Tile1 = Tile<64, 128, 2, 2, 2, 2>;                     // 4 waves 32x64, KBS 2
+using Tile2 = Tile<128, 128, 4, 2, 4, 2, 16>;                // as 0 on 16x16 MFMAs
+using Tile3 = Tile<128, 256, 4, 4, 4, 2>;                    // 16 waves 32x64
+using Tile4 = Tile<128, 128, 4, 2, 4, 2, 32, 1>;             // as 0, MFMAs first
+using Tile5 = Tile<64, 64, 2, 1, 8, 2, 32, 0, 4>;            // 4 K groups of 2 waves
+using Tile6 = Tile<64, 128, 2, 2, 8, 2, 32, 0, 2>;           // 2 K groups of 4 waves (LDS: one per CU)
+using Tile7 = Tile<64, 128, 2, 2, 4, 2, 32, 0, 2>;           // as 6, stages of 4
+using Tile8 = Tile<64, 192, 2, 3, 6, 2, 32, 1, 2>;           // 2 K groups of 6 waves, MFMAs first
+using Tile9 = Tile<128, 384, 4, 3, 3, 2, 32, 0, 1>;          // 12 waves 32x128, KBS 3
+
+template <class T>
+constexpr bool dims_match(int i) {
+  return T::BM == kTileDims[i].bm && T::BN == kTileDims[i].bn;
+}
+static_assert(dims_match<Tile0>(0) && dims_match<Tile1>(1) && dims_match<Tile2>(2) &&
+                  dims_match<Tile3>(3) && dims_match<Tile4>(4) && dims_match<Tile5>(5) &&
+                  dims_match<Tile6>(6) && dims_match<Tile7>(7) && dims_match<Tile8>(8) &&
+                  dims_match<Tile9>(9),
+              "tile table and q8_tilemap.h agree");
+
 const TileConfig kTiles[] = {
-    {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2>, 4>},       // 0: 8 waves 32x64, KBS 4
-    {64, 128, launch_tile<Tile<64, 128, 2, 2, 2, 2>, 4>},         // 1: 4 waves 32x64, KBS 2
-    {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2, 16>, 4>},   // 2: as 0 on 16x16 MFMAs
-    {128, 256, launch_tile<Tile<128, 256, 4, 4, 4, 2>, 4>},       // 3: 16 waves 32x64
-    {128, 128, launch_tile<Tile<128, 128, 4, 2, 4, 2, 32, 1>, 4>},   // 4: as 0, MFMAs first
-    {64, 64, launch_tile<Tile<64, 64, 2, 1, 8, 2, 32, 0, 4>, 4>},     // 5: 4 K groups of 2 waves
-    {64, 128, launch_tile<Tile<64, 128, 2, 2, 8, 2, 32, 0, 2>, 2>},   // 6: 2 K groups of 4 waves (LDS: one per CU)
-    {64, 128, launch_tile<Tile<64, 128, 2, 2, 4, 2, 32, 0, 2>, 4>},   // 7: as 6, stages of 4
-    {64, 192, launch_tile<Tile<64, 192, 2, 3, 6, 2, 32, 1, 2>, 3>},   // 8: 2 K groups of 6 waves, MFMAs first
-    {128, 384, launch_tile<Tile<128, 384, 4, 3, 3, 2, 32, 0, 1>, 3>},   // 9: 12 waves 32x128, KBS 3
+    {128, 128, launch_tile<Tile0, 4>}, {64, 128, launch_tile<Tile1, 4>},
+    {128, 128, launch_tile<Tile2, 4>}, {128, 256, launch_tile<Tile3, 4>},
+    {128, 128, launch_tile<Tile4, 4>}, {64, 64, launch_tile<Tile5, 4>},
+    {64, 128, launch_tile<Tile6, 2>},  {64, 128, launch_tile<Tile7, 4>},
+    {64, 192, launch_tile<Tile8, 3>},  {128, 384, launch_tile<Tile9, 3>},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+static_assert(kNumTiles == kNumTileDims, "tile table and q8_tilemap.h agree");
 
 bool tile_fits(int t, int64_t K) { return buffer_ranges_fit(kTiles[t].bm, kTiles[t].bn, K); }
 
@@ -1094,30 +1112,10 @@ int pick_tile(int64_t M, int64_t N, int64_t K) {
   if (forced >= 0 && log_enabled())
     fprintf(stderr, "q8: Q8_GEMM_TILE=%d ignored (no such tile, or K=%lld too large for it)\n",
             forced, static_cast<long long>(K));
-  // Grids of at least two 128x128 tiles per CU: 128x128 tiles with a
-  // wave's MFMAs issued ahead of its epilogues.  Smaller grids would leave
-  // SIMDs with one or two waves, too few to issue the epilogue at rate, so
-  // they take 64x128 or 64x64 tiles whose waves split each stage's blocks
-  // between two or four K groups (more waves for the same outputs):
-  // 64x192 tiles of 12 waves (one per CU) when N is whole 192-column tiles
-  // and they make 3/4 to 1 tile per CU; 64x128 tiles in stages of 4 blocks
-  // (two workgroups per CU) when they are more than one per CU, in stages of
-  // 8 (one per CU) when there are at least 3/4 as many as CUs, else 64x64
-  // tiles in four K groups.
-  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-  const int64_t t64 = ((M + 63) / 64) * ((N + 127) / 128);
-  const int64_t t192 = ((M + 63) / 64) * (N / 192);
-  // 128x384 tiles of 12 waves (one per CU, 32x128 per wave: a quarter fewer
-  // LDS reads per MFMA) when N is whole 384-column tiles and they fill
-  // whole rounds of the 256 CUs; otherwise the last round's idle CUs cost
-  // more than the 3 % they gain.
-  const int64_t t384 = ((M + 127) / 128) * (N / 384);
-  if (N % 384 == 0 && t384 >= 256 && t384 % 256 == 0) return 9;
-  if (t128 >= 512) return 4;
-  if (N % 192 == 0 && t192 >= 192 && t192 <= 256) return 8;
-  if (t64 > 256) return 7;
-  if (t64 >= 192) return 6;
-  return 5;}
+  // The automatic choice (q8_tilemap.h): by the grid's size and shape, and
+  // only among configurations whose buffer ranges hold K.
+  return choose_tile(M, N, K);
+}
 
 }  // namespace
 
@@ -1186,35 +1184,19 @@ hipError_t launch_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a
   if (log_enabled())
     fprintf(stderr, "q8: gated step M=%lld I=%lld K=%lld: matrix-core kernel, tile %d\n",
             static_cast<long long>(M), static_cast<long long>(I), static_cast<long long>(K), t);
+  const auto go = [&](auto launch) { return launch(M, N, K, q_a, d_a, w_packed, nullptr, N,
+                                                   stream, q_h, d_h); };
   switch (t) {
-    case 5:
-      return launch_tile_impl<Tile<64, 64, 2, 1, 8, 2, 32, 0, 4>, 4, true>(
-          M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
-    case 6:
-      return launch_tile_impl<Tile<64, 128, 2, 2, 8, 2, 32, 0, 2>, 2, true>(
-          M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
-    case 7:
-      return launch_tile_impl<Tile<64, 128, 2, 2, 4, 2, 32, 0, 2>, 4, true>(
-          M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
-    case 9:
-      return launch_tile_impl<Tile<128, 384, 4, 3, 3, 2, 32, 0, 1>, 3, true>(
-          M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
-    case 8:
-      return launch_tile_impl<Tile<64, 192, 2, 3, 6, 2, 32, 1, 2>, 3, true>(
-          M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
-    case 1:
-      return launch_tile_impl<Tile<64, 128, 2, 2, 2, 2>, 4, true>(M, N, K, q_a, d_a, w_packed,
-                                                                  nullptr, N, stream, q_h, d_h);
-    case 3:
-      return launch_tile_impl<Tile<128, 256, 4, 4, 4, 2>, 4, true>(M, N, K, q_a, d_a, w_packed,
-                                                                   nullptr, N, stream, q_h, d_h);
+    case 1: return go(launch_tile_impl<Tile1, 4, true>);
+    case 3: return go(launch_tile_impl<Tile3, 4, true>);
+    case 5: return go(launch_tile_impl<Tile5, 4, true>);
+    case 6: return go(launch_tile_impl<Tile6, 2, true>);
+    case 7: return go(launch_tile_impl<Tile7, 4, true>);
+    case 8: return go(launch_tile_impl<Tile8, 3, true>);
+    case 9: return go(launch_tile_impl<Tile9, 3, true>);
     case 0:
-    case 2:
-      return launch_tile_impl<Tile<128, 128, 4, 2, 4, 2>, 4, true>(M, N, K, q_a, d_a, w_packed,
-                                                                   nullptr, N, stream, q_h, d_h);
-    default:
-      return launch_tile_impl<Tile<128, 128, 4, 2, 4, 2, 32, 1>, 4, true>(
-          M, N, K, q_a, d_a, w_packed, nullptr, N, stream, q_h, d_h);
+    case 2: return go(launch_tile_impl<Tile0, 4, true>);
+    default: return go(launch_tile_impl<Tile4, 4, true>);
   }
 }
 

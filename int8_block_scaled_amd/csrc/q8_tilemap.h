@@ -83,4 +83,48 @@ inline bool buffer_ranges_fit(int64_t bm, int64_t bn, int64_t K) {
   return bm * K < kRange && bn * K < kRange;
 }
 
+// Output tile of each compiled matrix-core configuration, by index (the
+// kernels' table is checked against it at compile time).
+struct TileDims {
+  int bm, bn;
+};
+constexpr TileDims kTileDims[] = {
+    {128, 128},   // 0: 8 waves of 32x64
+    {64, 128},    // 1: 4 waves of 32x64
+    {128, 128},   // 2: as 0 on 16x16 MFMAs
+    {128, 256},   // 3: 16 waves of 32x64
+    {128, 128},   // 4: as 0, MFMAs first
+    {64, 64},     // 5: 4 K groups of 2 waves
+    {64, 128},    // 6: 2 K groups of 4 waves, stages of 8
+    {64, 128},    // 7: as 6, stages of 4
+    {64, 192},    // 8: 2 K groups of 6 waves
+    {128, 384},   // 9: 12 waves of 32x128
+};
+constexpr int kNumTileDims = static_cast<int>(sizeof(kTileDims) / sizeof(kTileDims[0]));
+
+// The configuration the launcher takes for an M x N x K product (M > 64):
+//  - 128x384 tiles when N is whole 384-column tiles and they fill whole
+//    rounds of the 256 CUs (one workgroup per CU);
+//  - 128x128 tiles when there are at least two per CU;
+//  - 64x192 tiles when N is whole 192-column tiles and they make 3/4 to 1
+//    tile per CU;
+//  - 64x128 tiles in stages of 4 (two workgroups per CU) when they are more
+//    than one per CU, in stages of 8 (one per CU) from 3/4 to 1 per CU;
+//  - else 64x64 tiles in four K groups.
+// A candidate whose 32-bit buffer ranges cannot hold K is passed over (the
+// 128x128 and smaller tiles hold every K up to 2^24).
+inline int choose_tile(int64_t M, int64_t N, int64_t K) {
+  auto fits = [K](int t) { return buffer_ranges_fit(kTileDims[t].bm, kTileDims[t].bn, K); };
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t t64 = ((M + 63) / 64) * ((N + 127) / 128);
+  const int64_t t192 = ((M + 63) / 64) * (N / 192);
+  const int64_t t384 = ((M + 127) / 128) * (N / 384);
+  if (N % 384 == 0 && t384 >= 256 && t384 % 256 == 0 && fits(9)) return 9;
+  if (t128 >= 512) return 4;
+  if (N % 192 == 0 && t192 >= 192 && t192 <= 256 && fits(8)) return 8;
+  if (t64 > 256) return 7;
+  if (t64 >= 192) return 6;
+  return 5;
+}
+
 }  // namespace q8

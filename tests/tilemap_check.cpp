@@ -1,7 +1,8 @@
 // Host-only check of the matrix-core product's workgroup orders
 // (int8_block_scaled_amd/csrc/q8_tilemap.h): every order the launcher may
 // use is a bijection from workgroup ids onto the tile grid, the automatic
-// choice is always admissible, and inadmissible orders are rejected.
+// choice is always admissible, and inadmissible orders are rejected; the
+// automatic tile choice always fits its 32-bit buffer ranges.
 // Prints one line per failure and exits non-zero if there is any.
 #include <cstdio>
 #include <vector>
@@ -52,6 +53,34 @@ int main() {
         const int order = q8::choose_order(tm, tn, bm, K);
         if (!q8::order_admissible(order, tm, tn)) fail("chosen order not admissible", tm, tn, order);
       }
+  }
+  // The automatic tile choice: always a configuration whose 32-bit buffer
+  // ranges hold K, for K up to 2^24; and the expected tile on the benchmark
+  // workloads.
+  long tiles_checked = 0;
+  for (long long M : {65LL, 96LL, 128LL, 509LL, 512LL, 1024LL, 2048LL, 4096LL, 8192LL, 32768LL})
+    for (long long N : {64LL, 384LL, 4096LL, 5120LL, 6144LL, 12288LL, 17408LL, 24576LL, 98304LL})
+      for (long long K : {32LL, 4096LL, 17408LL, (1LL << 22), 11184800LL, 11184832LL, (1LL << 24)}) {
+        const int t = q8::choose_tile(M, N, K);
+        ++tiles_checked;
+        if (t < 0 || t >= q8::kNumTileDims) {
+          fail("tile index out of the table", static_cast<int>(M), static_cast<int>(N), t);
+          continue;
+        }
+        if (!q8::buffer_ranges_fit(q8::kTileDims[t].bm, q8::kTileDims[t].bn, K))
+          fail("chosen tile's buffer ranges cannot hold K", static_cast<int>(M),
+               static_cast<int>(K >> 10), t);
+      }
+  const struct { long long M, N, K; int tile; } want[] = {
+      {2048, 12288, 4096, 9},  {8192, 17408, 5120, 4}, {8192, 5120, 17408, 4},
+      {512, 6144, 4096, 8},    {509, 6144, 4096, 8},   {512, 4096, 4096, 6},
+      {512, 24576, 4096, 9},   {512, 4096, 12288, 6},  {128, 4096, 4096, 5},
+      // the 128x384 tile cannot hold K >= 2^32 / 384: the 128x128 tile instead
+      {2048, 12288, 1LL << 24, 4}};
+  for (auto& w : want) {
+    const int t = q8::choose_tile(w.M, w.N, w.K);
+    if (t != w.tile) fail("unexpected tile for a workload", static_cast<int>(w.M),
+                          static_cast<int>(w.N), t);
   }
   // cases that break the map if let through (tile index past the grid, or a
   // division by zero), which the launcher must therefore reject
