@@ -307,10 +307,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Widen the stage's scales and store them: d_a as binary32, d_w as the pair
 // (d_w, -1.5*2^23*d_w) the epilogue consumes.
+//
+// d_a is stored in groups of four rows rotated by one slot (row 4g + t at
+// slot 4g + (t + 3) % 4).  A lane reads a group with one 16-byte load into
+// four consecutive VGPRs, and its accumulators of the same four rows are
+// consecutive VGPRs too; both tuples start on an even register, so unrotated
+// the scale and the accumulator of row r always share a VGPR bank (register
+// index mod 4), and the epilogue's v_fmac_f32, which reads both, then issues
+// at about half the rate when two or more waves of a SIMD interleave
+// (measured on gfx950: a block of one MFMA and 32 FMAs per tile took 108 ->
+// 92 cycles per MFMA at four waves per SIMD, 113 -> 98 at two).  Rotated,
+// the two banks always differ.
 template <class T>
 __device__ __forceinline__ void store_scales(int tid, uint8_t* buf, const uint16_t (&as_r)[T::kASc],
                                              const uint16_t (&bs_r)[T::kBSc]) {
-  const uint32_t as = lds_addr(buf + T::kAq + T::kBq) + tid * 4;
+  static_assert(T::kThreads % 4 == 0 && T::BM % 4 == 0, "a thread keeps its row mod 4");
+  const uint32_t as = lds_addr(buf + T::kAq + T::kBq) + (tid & ~3) * 4 + ((tid + 3) & 3) * 4;
   const uint32_t bs = lds_addr(buf + T::kAq + T::kBq + T::kAs) + tid * 8;
   static_for<T::kASc>([&](auto i_) __attribute__((always_inline)) {
     constexpr int i = decltype(i_)::value;
@@ -370,10 +382,11 @@ __device__ __forceinline__ void compute_stage(uint32_t base_a, uint32_t base_as,
       float av[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        av[4 * q + 0] = __int_as_float(avq[i][q].x);
-        av[4 * q + 1] = __int_as_float(avq[i][q].y);
-        av[4 * q + 2] = __int_as_float(avq[i][q].z);
-        av[4 * q + 3] = __int_as_float(avq[i][q].w);
+        // groups are stored rotated by one (store_scales): row 4q + t at slot (t + 3) % 4
+        av[4 * q + 0] = __int_as_float(avq[i][q].w);
+        av[4 * q + 1] = __int_as_float(avq[i][q].x);
+        av[4 * q + 2] = __int_as_float(avq[i][q].y);
+        av[4 * q + 3] = __int_as_float(avq[i][q].z);
       }
       if constexpr (T::PIPE) {
         // All of the row tile's MFMAs first: the later ones run on the matrix
@@ -494,7 +507,7 @@ __device__ __forceinline__ void compute_stage16(uint32_t base_a, uint32_t base_a
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float y = fmaf(__int_as_float(pu[r]), cur.ws[j].x, cur.ws[j].y);
-      acc[i][j][r] = fmaf(y, cur.as[i][r], acc[i][j][r]);
+      acc[i][j][r] = fmaf(y, cur.as[i][(r + 3) & 3], acc[i][j][r]);   // rotated groups
     }
     asm volatile("" : "+v"(acc[i][j]), "+v"(bias));
   });
@@ -759,6 +772,10 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
 // ---------------------------------------------------------------------------
 constexpr int64_t kSmallMaxM = 64;
 
+// Slot of row r in its group of four when d_a is stored rotated by one (see
+// store_scales: keeps a row's scale and accumulator in different VGPR banks).
+__device__ __forceinline__ int rot4(int r) { return (r & ~3) | ((r + 3) & 3); }
+
 template <int MT, int L, int W, int X>
 __global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
     const int8_t* __restrict__ q_a, const uint16_t* __restrict__ d_a,
@@ -863,7 +880,7 @@ __global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
         uint16_t dbits;
         quantize8(v, lo, hi, dbits);   // all lanes take part (lane exchanges)
         *reinterpret_cast<uint2*>(slot + row * kRow + b * kQK + sub * 8) = make_uint2(lo, hi);
-        if (sub == 0) sslot[((row >> 5) * L + b) * 32 + (row & 31)] = f16_bits_to_f32(dbits);
+        if (sub == 0) sslot[((row >> 5) * L + b) * 32 + rot4(row & 31)] = f16_bits_to_f32(dbits);
         if (store_q && row < M && c + b < kb1) {
           *reinterpret_cast<uint2*>(q_out + row * K + (c + b) * kQK + sub * 8) =
               make_uint2(lo, hi);
@@ -925,7 +942,7 @@ __global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
 #pragma unroll
       for (int u = 0; u < kScs / 64; ++u) {
         const int sc = u * 64 + lane, row = sc / L, b = sc % L;
-        sslot[((row >> 5) * L + b) * 32 + (row & 31)] = f16_bits_to_f32(xs[u]);
+        sslot[((row >> 5) * L + b) * 32 + rot4(row & 31)] = f16_bits_to_f32(xs[u]);
       }
     }
 #pragma unroll
@@ -953,7 +970,7 @@ __global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float y = fmaf(__int_as_float(p[r]), wp[j].x, wp[j].y);
-            acc[i][j][r] = fmaf(y, da[r >> 2][r & 3], acc[i][j][r]);
+            acc[i][j][r] = fmaf(y, da[r >> 2][(r + 3) & 3], acc[i][j][r]);   // rot4 groups
           }
         }
       }
