@@ -638,12 +638,23 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   constexpr int NBUF = T::NBUF;
   const int nstages = static_cast<int>((KB + KBS - 1) / KBS);
   uint16_t as_r[T::kASc], bs_r[T::kBSc];
-  if (NBUF == 2) load_scales<T>(rs, lo, 0, as_r, bs_r);   // (NBUF > 2: loaded at t = -2)
-  for (int t = -(NBUF - 1); t < 0; ++t) {
-    issue_quants<T, 0, T::kDmaOps>(rs, lo, wave, (t + NBUF - 1) * KBS,
-                                   smem + ((t + NBUF - 1) % NBUF) * T::kStage);
-    if (t == -1) store_scales<T>(tid, smem, as_r, bs_r);                  // stage 0
-    if (t + 2 >= 0) load_scales<T>(rs, lo, (t + 2) * KBS, as_r, bs_r);
+  if constexpr (NBUF == 2) {
+    // Stage 0's quants and scales and stage 1's scales, all in flight
+    // together: stage 1's scales go to the loop's registers, so storing
+    // stage 0's waits only for its own loads (one memory round trip for the
+    // prologue instead of two).
+    uint16_t as0[T::kASc], bs0[T::kBSc];
+    load_scales<T>(rs, lo, 0, as0, bs0);
+    issue_quants<T, 0, T::kDmaOps>(rs, lo, wave, 0, smem);
+    load_scales<T>(rs, lo, KBS, as_r, bs_r);
+    store_scales<T>(tid, smem, as0, bs0);
+  } else {
+    for (int t = -(NBUF - 1); t < 0; ++t) {
+      issue_quants<T, 0, T::kDmaOps>(rs, lo, wave, (t + NBUF - 1) * KBS,
+                                     smem + ((t + NBUF - 1) % NBUF) * T::kStage);
+      if (t == -1) store_scales<T>(tid, smem, as_r, bs_r);                  // stage 0
+      if (t + 2 >= 0) load_scales<T>(rs, lo, (t + 2) * KBS, as_r, bs_r);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
