@@ -103,8 +103,15 @@ constexpr TileDims kTileDims[] = {
 constexpr int kNumTileDims = static_cast<int>(sizeof(kTileDims) / sizeof(kTileDims[0]));
 
 // The configuration the launcher takes for an M x N x K product (M > 64):
-//  - 128x384 tiles when N is whole 384-column tiles and they fill whole
-//    rounds of the 256 CUs (one workgroup per CU);
+//  - 128x384 tiles when they make at least one round of the 256 CUs (one
+//    workgroup per CU) and the work they waste -- the unused columns of a
+//    ragged last column tile, the unused rows of a ragged last row tile and
+//    the idle CUs of a partial last round -- leaves them within 10 % of the
+//    128x128 tiles' useful fraction (which waste the same way, at two
+//    workgroups per CU); per launch round the 128x384 tile does about 10 %
+//    more work per unit time than the 128x128 tile (measured on gfx950:
+//    M8192 N17408 K5120 1745 vs 1880 us, 11.5 rounds; M8192 N5120 K17408
+//    1830 vs 1802 us, 3.5 rounds and a third of a column tile idle);
 //  - 128x128 tiles when there are at least two per CU;
 //  - 64x192 tiles when N is whole 192-column tiles and they make 3/4 to 1
 //    tile per CU;
@@ -113,13 +120,24 @@ constexpr int kNumTileDims = static_cast<int>(sizeof(kTileDims) / sizeof(kTileDi
 //  - else 64x64 tiles in four K groups.
 // A candidate whose 32-bit buffer ranges cannot hold K is passed over (the
 // 128x128 and smaller tiles hold every K up to 2^24).
+// Useful fraction of a launch of bm x bn tiles, `slots` resident at a time:
+// the product's outputs over the outputs of the tiles' whole rounds.
+inline double launch_fill(int64_t M, int64_t N, int bm, int bn, int64_t slots) {
+  const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
+  const int64_t rounds = (tm * tn + slots - 1) / slots;
+  return static_cast<double>(M) * static_cast<double>(N) /
+         (static_cast<double>(rounds * slots) * bm * bn);
+}
+
 inline int choose_tile(int64_t M, int64_t N, int64_t K) {
   auto fits = [K](int t) { return buffer_ranges_fit(kTileDims[t].bm, kTileDims[t].bn, K); };
   const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
   const int64_t t64 = ((M + 63) / 64) * ((N + 127) / 128);
   const int64_t t192 = ((M + 63) / 64) * (N / 192);
-  const int64_t t384 = ((M + 127) / 128) * (N / 384);
-  if (N % 384 == 0 && t384 >= 256 && t384 % 256 == 0 && fits(9)) return 9;
+  const int64_t t384 = ((M + 127) / 128) * ((N + 383) / 384);
+  if (t384 >= 256 && fits(9) &&
+      1.1 * launch_fill(M, N, 128, 384, 256) >= launch_fill(M, N, 128, 128, 512))
+    return 9;
   if (t128 >= 512) return 4;
   if (N % 192 == 0 && t192 >= 192 && t192 <= 256 && fits(8)) return 8;
   if (t64 > 256) return 7;

@@ -72,7 +72,8 @@ int main() {
                static_cast<int>(K >> 10), t);
       }
   const struct { long long M, N, K; int tile; } want[] = {
-      {2048, 12288, 4096, 9},  {8192, 17408, 5120, 4}, {8192, 5120, 17408, 4},
+      {2048, 12288, 4096, 9},  {8192, 17408, 5120, 9}, {8192, 5120, 17408, 4},
+      {2048, 17408, 5120, 9},  {2048, 8192, 8192, 4},  {4096, 8192, 8192, 4},
       {512, 6144, 4096, 8},    {509, 6144, 4096, 8},   {512, 4096, 4096, 6},
       {512, 24576, 4096, 9},   {512, 4096, 12288, 6},  {128, 4096, 4096, 5},
       // the 128x384 tile cannot hold K >= 2^32 / 384: the 128x128 tile instead
