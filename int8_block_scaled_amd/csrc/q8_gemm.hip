@@ -1147,8 +1147,8 @@ using Tile2 = Tile<128, 128, 4, 2, 4, 2, 16>;                // as 0 on 16x16 MF
 using Tile3 = Tile<128, 256, 4, 4, 4, 2>;                    // 16 waves 32x64
 using Tile4 = Tile<128, 128, 4, 2, 4, 2, 32, 1>;             // as 0, MFMAs first
 using Tile5 = Tile<64, 64, 2, 1, 8, 2, 32, 0, 4>;            // 4 K groups of 2 waves
-using Tile6 = Tile<64, 128, 2, 2, 8, 2, 32, 0, 2>;           // 2 K groups of 4 waves (LDS: one per CU)
-using Tile7 = Tile<64, 128, 2, 2, 4, 2, 32, 0, 2>;           // as 6, stages of 4
+using Tile6 = Tile<64, 128, 2, 2, 8, 2, 32, 1, 2>;           // 2 K groups of 4 waves, MFMAs first (LDS: one per CU)
+using Tile7 = Tile<64, 128, 2, 2, 4, 2, 32, 0, 2>;           // 2 K groups of 4 waves, stages of 4
 using Tile8 = Tile<64, 192, 2, 3, 6, 2, 32, 1, 2>;           // 2 K groups of 6 waves, MFMAs first
 using Tile9 = Tile<128, 384, 4, 3, 3, 2, 32, 0, 1>;          // 12 waves 32x128, KBS 3
 

@@ -95,8 +95,8 @@ constexpr TileDims kTileDims[] = {
     {128, 256},   // 3: 16 waves of 32x64
     {128, 128},   // 4: as 0, MFMAs first
     {64, 64},     // 5: 4 K groups of 2 waves
-    {64, 128},    // 6: 2 K groups of 4 waves, stages of 8
-    {64, 128},    // 7: as 6, stages of 4
+    {64, 128},    // 6: 2 K groups of 4 waves, stages of 8, MFMAs first
+    {64, 128},    // 7: 2 K groups of 4 waves, stages of 4
     {64, 192},    // 8: 2 K groups of 6 waves
     {128, 384},   // 9: 12 waves of 32x128
 };
