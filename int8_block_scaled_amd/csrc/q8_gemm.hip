@@ -45,8 +45,10 @@
 // Occupancy.  The epilogue issues at rate only with several waves per SIMD
 // (one wave alone issues an FMA every ~4.6 clocks).  Large grids get them
 // from 128x384 tiles of twelve 32x128 waves (one workgroup per CU, three
-// waves per SIMD; a 32x128 wave tile reads its activation scales once for
-// four MFMAs) when N and the grid suit them, else from 128x128 tiles, two
+// waves per SIMD, whose priorities rotate block by block because a SIMD
+// interleaves only two waves at a time; a 32x128 wave tile reads its
+// activation scales once for four MFMAs) when the grid suits them (see
+// choose_tile in q8_tilemap.h), else from 128x128 tiles, two
 // workgroups of eight waves per CU, each wave issuing its MFMAs ahead of
 // their epilogues.  Grids with too few tiles split every stage's blocks
 // between K groups of waves instead, and add the groups' partial sums
