@@ -1075,15 +1075,15 @@ __global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
 #endif
 }
 
-// 8 waves (two per SIMD: up to 190 registers), chunks of 8 blocks for one
-// 32-row activation tile, 4 for two.  16 waves would cap a wave at 128
-// registers, below what the one-tile chunk needs without spilling.
+// 8 waves (two per SIMD: up to 256 registers), chunks of 4 blocks.  16 waves
+// would cap a wave at 128 registers, below what a chunk needs without
+// spilling (149 at one 32-row activation tile, 191 at two).
 template <int MT, int X>
 hipError_t launch_small(int64_t M, int64_t N, int64_t K, const int8_t* q_a, const uint16_t* d_a,
                         const void* x, int64_t ldx, int8_t* q_out, uint16_t* d_out,
                         const uint8_t* w_packed, float* C, int64_t ldc, hipStream_t stream) {
   constexpr int W = 8;
-  constexpr int L = MT == 1 ? 8 : 4;
+  constexpr int L = 4;   // (8 at one tile measured 5-6 % slower, 2 at two tiles 2-10 %)
   const int64_t KB = K / kQK;
   const int64_t NG = num_groups(N);
   const uint16_t* ws = reinterpret_cast<const uint16_t*>(w_packed + NG * KB * kGroupBlockBytes);
