@@ -109,10 +109,15 @@ struct Tile {
   static constexpr int kWavesT = WAVES_M * WAVES_N;            // waves of one K group
   static constexpr int kThreads = kWavesT * KSPLIT * 64;
   static constexpr int kWaves = kWavesT * KSPLIT;
-  // twelve waves, one workgroup per CU: three waves per SIMD (wave w runs on
-  // SIMD w % 4), whose priorities compute_stage rotates
-  static constexpr bool kRotatePrio = kWaves == 12;
-  static_assert(!kRotatePrio || NB == 3, "priorities rotate over the three blocks of a stage");
+  // Priorities that compute_stage rotates block by block (wave w runs on
+  // SIMD w % 4): twelve waves, one workgroup per CU, three per SIMD (period
+  // 3); eight waves of one K group, two workgroups per CU, so two of each
+  // workgroup's on each SIMD (period 2: measured 1-2 % faster on the large
+  // grids that take these tiles; with one workgroup per CU, as the K-group
+  // tiles run, it measured 4-6 % slower, so those keep fixed priorities).
+  static constexpr bool kRotatePrio = kWaves == 12 || (kWaves == 8 && KSPLIT == 1);
+  static constexpr int kPrioPeriod = kWaves == 12 ? 3 : 2;
+  static_assert(!kRotatePrio || NB % kPrioPeriod == 0, "priorities rotate over whole stages");
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // per-wave tile
   static constexpr int TM = WM / MF, TN = WN / MF;             // MFMA tiles per wave
   static constexpr int kSlots = 2 * KBS;                       // 16-byte slots per row per stage
@@ -344,7 +349,7 @@ __device__ __forceinline__ void store_scales(int tid, uint8_t* buf, const uint16
   });
 }
 
-// Wave priority for three waves per SIMD.  A SIMD interleaves the vector
+// Wave priorities (Tile::kRotatePrio).  A SIMD interleaves the vector
 // instructions of two waves at a time; with three resident, the two of
 // higher priority (or, at equal priority, the older two) take nearly every
 // issue slot and the third runs only when one of them stalls.  Measured on
@@ -353,7 +358,9 @@ __device__ __forceinline__ void store_scales(int tid, uint8_t* buf, const uint16
 // barrier the other two then wait for it.  Rotating the priorities block by
 // block, so that each wave is the low one for a third of the blocks, keeps
 // the three together: 130 -> 118 cycles per MFMA in that probe with LDS
-// operand reads and a barrier every three blocks.
+// operand reads and a barrier every three blocks.  The 128x128 tiles, two
+// workgroups of eight waves per CU, alternate the two waves of each
+// workgroup on a SIMD the same way.
 // The branch on p (0, 1 or 2; s_setprio takes only an immediate) stays
 // inside one asm statement, so it splits no basic block of the compiled loop.
 __device__ __forceinline__ void set_wave_prio(int p) {
@@ -387,7 +394,12 @@ __device__ __forceinline__ void compute_stage(uint32_t base_a, uint32_t base_as,
   constexpr int TM = T::TM, TN = T::TN, BM = T::BM, BN = T::BN;
   static_for<T::NB>([&](auto kb_) __attribute__((always_inline)) {
     constexpr int kb = decltype(kb_)::value;
-    if constexpr (T::kRotatePrio) set_wave_prio(prio0 + kb < 3 ? prio0 + kb : prio0 + kb - 3);
+    if constexpr (T::kRotatePrio) {
+      if constexpr (T::kPrioPeriod == 3)
+        set_wave_prio(prio0 + kb < 3 ? prio0 + kb : prio0 + kb - 3);
+      else
+        set_wave_prio((prio0 + kb) & 1);
+    }
     v4i af[TM], avq[TM][4], bf[TN];
     v2f wp[TN];
     static_for<TM>([&](auto i_) __attribute__((always_inline)) {
@@ -614,7 +626,8 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   const uint32_t lane_bs =
       T::kAq + T::kBq + T::kAs + kofs * BN * 8 + (wn0 + (T::MF == 32 ? l32 : l16)) * 8;
   const uint32_t lds_base = lds_addr(smem);
-  // the wave's place among the three waves of its SIMD (wave w runs on SIMD w % 4)
+  // the wave's place among its workgroup's waves on its SIMD (wave w runs on
+  // SIMD w % 4)
   const int prio_slot = __builtin_amdgcn_readfirstlane(wave >> 2);
 
   using acc_t = std::conditional_t<T::MF == 32, v16f, v4f>;
