@@ -131,7 +131,11 @@ struct Tile {
   static constexpr int kAInst = BM * kSlots / 64 / kWaves;
   static constexpr int kBInst = (BN / kGroupRows) * 2 * KBS / kWaves;
   static constexpr int kASc = (BM * KBS + kThreads - 1) / kThreads;
-  static constexpr int kBSc = (BN * KBS + kThreads - 1) / kThreads;
+  // Weight scales go in pairs of adjacent columns (one dword load and one
+  // 16-byte LDS write per pair) when there are more than one per thread.
+  static constexpr bool kBPair = BN * KBS > kThreads;
+  static constexpr int kBPer = kBPair ? 2 : 1;                 // columns per load
+  static constexpr int kBSc = (BN * KBS / kBPer + kThreads - 1) / kThreads;
   static_assert(MF == 32 || MF == 16, "MFMA shape");
   static_assert(WM % MF == 0 && WN % MF == 0, "wave tile must be a multiple of the MFMA tile");
   static_assert(BN % kGroupRows == 0, "BN must cover whole 64-row groups");
@@ -189,6 +193,10 @@ template <int OFF>
 __device__ __forceinline__ void lds_write_b64(uint32_t base, v2f v) {
   asm volatile("ds_write_b64 %0, %1 offset:%2" : : "v"(base), "v"(v), "i"(OFF) : "memory");
 }
+template <int OFF>
+__device__ __forceinline__ void lds_write_b128(uint32_t base, v4f v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(base), "v"(v), "i"(OFF) : "memory");
+}
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // Ties a value to the preceding wait so that no use of it moves above it.
 template <class V>
@@ -220,7 +228,7 @@ struct LaneOffsets {
   uint32_t a[T::kAInst];      // activation quant loads (into LDS)
   uint32_t b[T::kBInst];      // weight quant loads (into LDS)
   uint32_t sa[T::kASc];       // activation scale loads
-  uint32_t sb[T::kBSc];       // weight scale loads
+  uint32_t sb[T::kBSc];       // weight scale loads (of kBPer adjacent columns)
   int lim_a[T::kASc];         // the scale load is in range while kb0 < lim
   int lim_b[T::kBSc];
 };
@@ -250,7 +258,7 @@ __device__ __forceinline__ void lane_offsets(LaneOffsets<T>& o, int tid, int wav
   }
 #pragma unroll
   for (int i = 0; i < T::kBSc; ++i) {
-    const uint32_t idx = i * T::kThreads + tid;
+    const uint32_t idx = T::kBPer * (i * T::kThreads + tid);   // first column of the load
     const uint32_t n = idx % BN, kbl = idx / BN;
     o.sb[i] = (((n / kGroupRows) * KB + kbl) * kGroupRows + n % kGroupRows) * 2;
     o.lim_b[i] = idx < BN * KBS ? static_cast<int>(KB - kbl) : 0;
@@ -297,7 +305,7 @@ __device__ __forceinline__ void issue_quants(const Rsrc& r, const LaneOffsets<T>
 // zero through an out-of-range offset).
 template <class T>
 __device__ __forceinline__ void load_scales(const Rsrc& r, const LaneOffsets<T>& o, int kb0,
-                                            uint16_t (&as_r)[T::kASc], uint16_t (&bs_r)[T::kBSc]) {
+                                            uint16_t (&as_r)[T::kASc], uint32_t (&bs_r)[T::kBSc]) {
 #if __HIP_DEVICE_COMPILE__
   kb0 = __builtin_amdgcn_readfirstlane(kb0);
 #pragma unroll
@@ -306,8 +314,14 @@ __device__ __forceinline__ void load_scales(const Rsrc& r, const LaneOffsets<T>&
                                                    static_cast<uint32_t>(kb0 * 2), 0);
 #pragma unroll
   for (int i = 0; i < T::kBSc; ++i)
-    bs_r[i] = __builtin_amdgcn_raw_buffer_load_b16(r.rsb, kb0 < o.lim_b[i] ? o.sb[i] : kOutOfRange,
-                                                   static_cast<uint32_t>(kb0 * kGroupRows * 2), 0);
+    if constexpr (T::kBPair)
+      bs_r[i] = __builtin_amdgcn_raw_buffer_load_b32(
+          r.rsb, kb0 < o.lim_b[i] ? o.sb[i] : kOutOfRange,
+          static_cast<uint32_t>(kb0 * kGroupRows * 2), 0);
+    else
+      bs_r[i] = __builtin_amdgcn_raw_buffer_load_b16(
+          r.rsb, kb0 < o.lim_b[i] ? o.sb[i] : kOutOfRange,
+          static_cast<uint32_t>(kb0 * kGroupRows * 2), 0);
 #endif
 }
 
@@ -331,10 +345,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the two banks always differ.
 template <class T>
 __device__ __forceinline__ void store_scales(int tid, uint8_t* buf, const uint16_t (&as_r)[T::kASc],
-                                             const uint16_t (&bs_r)[T::kBSc]) {
+                                             const uint32_t (&bs_r)[T::kBSc]) {
   static_assert(T::kThreads % 4 == 0 && T::BM % 4 == 0, "a thread keeps its row mod 4");
   const uint32_t as = lds_addr(buf + T::kAq + T::kBq) + (tid & ~3) * 4 + ((tid + 3) & 3) * 4;
-  const uint32_t bs = lds_addr(buf + T::kAq + T::kBq + T::kAs) + tid * 8;
+  const uint32_t bs = lds_addr(buf + T::kAq + T::kBq + T::kAs) + tid * 8 * T::kBPer;
   static_for<T::kASc>([&](auto i_) __attribute__((always_inline)) {
     constexpr int i = decltype(i_)::value;
     if (i * T::kThreads + tid < T::BM * T::KBS)
@@ -342,9 +356,14 @@ __device__ __forceinline__ void store_scales(int tid, uint8_t* buf, const uint16
   });
   static_for<T::kBSc>([&](auto i_) __attribute__((always_inline)) {
     constexpr int i = decltype(i_)::value;
-    if (i * T::kThreads + tid < T::BN * T::KBS) {
-      const float w = f16_bits_to_f32(bs_r[i]);
-      lds_write_b64<i * T::kThreads * 8>(bs, v2f{w, -kBias * w});
+    if (T::kBPer * (i * T::kThreads + tid) < T::BN * T::KBS) {
+      const float w0 = f16_bits_to_f32(static_cast<uint16_t>(bs_r[i]));
+      if constexpr (T::kBPair) {
+        const float w1 = f16_bits_to_f32(static_cast<uint16_t>(bs_r[i] >> 16));
+        lds_write_b128<i * T::kThreads * 16>(bs, v4f{w0, -kBias * w0, w1, -kBias * w1});
+      } else {
+        lds_write_b64<i * T::kThreads * 8>(bs, v2f{w0, -kBias * w0});
+      }
     }
   });
 }
@@ -652,13 +671,15 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   // remain": loads complete in issue order.
   constexpr int NBUF = T::NBUF;
   const int nstages = static_cast<int>((KB + KBS - 1) / KBS);
-  uint16_t as_r[T::kASc], bs_r[T::kBSc];
+  uint16_t as_r[T::kASc];
+  uint32_t bs_r[T::kBSc];
   if constexpr (NBUF == 2) {
     // Stage 0's quants and scales and stage 1's scales, all in flight
     // together: stage 1's scales go to the loop's registers, so storing
     // stage 0's waits only for its own loads (one memory round trip for the
     // prologue instead of two).
-    uint16_t as0[T::kASc], bs0[T::kBSc];
+    uint16_t as0[T::kASc];
+    uint32_t bs0[T::kBSc];
     load_scales<T>(rs, lo, 0, as0, bs0);
     issue_quants<T, 0, T::kDmaOps>(rs, lo, wave, 0, smem);
     load_scales<T>(rs, lo, KBS, as_r, bs_r);
