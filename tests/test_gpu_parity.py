@@ -85,6 +85,23 @@ def test_quantize_guard_bands(orc, dtype, M, K):
     assert np.array_equal(qh[1:M + 1], qr) and np.array_equal(dh[1:M + 1], dr)
 
 
+def test_quantize_rows_past_grid_limit(orc):
+    """More row groups than a launch grid holds in y (65535): the workgroups
+    loop over further groups, and a ragged last group stops at M."""
+    M, K = 4 * 65535 + 4 * 37 + 3, 64
+    r = np.random.default_rng(41)
+    x = (r.standard_normal((M, K)) * 2.0 ** r.uniform(-8, 8, (M, 1))).astype(np.float32)
+    xs = workloads.f32_to_bf16_bits(x)
+    say("quantize bf16 M=%d K=%d (rows past the grid's y limit)" % (M, K))
+    qbuf = torch.full((M + 1, K), 77, dtype=torch.int8, device=DEV)
+    dbuf = torch.full((M + 1, K // 32), 3.0, dtype=torch.float16, device=DEV)
+    q8.q8_quantize_act(x_to_dev(xs), q=qbuf[:M], d=dbuf[:M])
+    qh, dh = qbuf.cpu().numpy(), d_bits(dbuf)
+    assert np.all(qh[M] == 77) and np.all(dh[M] == 0x4200), "written past the last row"
+    qr, dr = orc.quantize_rows(xs)
+    assert np.array_equal(qh[:M], qr) and np.array_equal(dh[:M], dr)
+
+
 QUANT_LAYERS = [workloads.TINY, workloads.DECODE_M4, workloads.PREFILL, workloads.LARGE_UP,
                 workloads.LARGE_DOWN] + workloads.sweep(509)[::3]
 
