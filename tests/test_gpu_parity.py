@@ -86,8 +86,8 @@ def test_quantize_guard_bands(orc, dtype, M, K):
 
 
 def test_quantize_rows_past_grid_limit(orc):
-    """More row groups than a launch grid holds in y (65535): the workgroups
-    loop over further groups, and a ragged last group stops at M."""
+    """More rows than a launch grid holds in y (65535): the workgroups loop
+    over further rows and stop at M."""
     M, K = 4 * 65535 + 4 * 37 + 3, 64
     r = np.random.default_rng(41)
     x = (r.standard_normal((M, K)) * 2.0 ** r.uniform(-8, 8, (M, 1))).astype(np.float32)
