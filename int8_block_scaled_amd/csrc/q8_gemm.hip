@@ -920,120 +920,25 @@ __global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) bias[r] = kBiasBits;
 
-  for (int c = kb0; c < kb1; c += L) {
-    v4i wv[L][2];
-    uint16_t wsc[L][2];
-    // Raw activations (X != 0): item t = u*64 + lane is row t / (4L), block
-    // (t / 4) % L, values 8*(t % 4) .. +8 of it, so four lanes hold a block
-    // and 4L consecutive lanes a contiguous run of a row.  The first batch of
-    // items is loaded before the weights, the rest after.
-    constexpr int kItems = MT * 32 * L * 4;
-    constexpr int kPB = X == 1 ? 4 : 8;   // items per lane per batch: 32 registers
-    constexpr int kBatches = X == 0 ? 1 : kItems / 64 / kPB;
-    static_assert(X == 0 || kItems % (64 * kPB) == 0, "whole batches");
-    v4i raw[kPB][kEsz / 2];
-    auto load_batch = [&](int bt) {
-#pragma unroll
-      for (int e = 0; e < kPB; ++e) {
-        const int t = (bt * kPB + e) * 64 + lane;
-        const int row = t / (4 * L), b = (t / 4) % L, sub = t % 4;
-        const uint32_t off =
-            c + b < kb1 ? static_cast<uint32_t>((row * ldx + (c + b) * kQK + sub * 8) * kEsz)
-                        : kOutOfRange;
-#pragma unroll
-        for (int h = 0; h < kEsz / 2; ++h)
-          raw[e][h] = __builtin_amdgcn_raw_buffer_load_b128(
-              ra, off == kOutOfRange ? kOutOfRange : off + 16 * h, 0, 0);
-      }
-    };
-    auto quantize_batch = [&](int bt) {
-#pragma unroll
-      for (int e = 0; e < kPB; ++e) {
-        const int t = (bt * kPB + e) * 64 + lane;
-        const int row = t / (4 * L), b = (t / 4) % L, sub = t % 4;
-        float v[8];
-        if constexpr (X == 1) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[4 * h + q] = __int_as_float(raw[e][h][q]);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t w = static_cast<uint32_t>(raw[e][0][q]);
-            v[2 * q] = __uint_as_float(w << 16);
-            v[2 * q + 1] = __uint_as_float(w & 0xffff0000u);
-          }
-        }
-        uint32_t lo, hi;
-        uint16_t dbits;
-        quantize8(v, lo, hi, dbits);   // all lanes take part (lane exchanges)
-        *reinterpret_cast<uint2*>(slot + row * kRow + b * kQK + sub * 8) = make_uint2(lo, hi);
-        if (sub == 0) sslot[((row >> 5) * L + b) * 32 + rot4(row & 31)] = f16_bits_to_f32(dbits);
-        if (store_q && row < M && c + b < kb1) {
-          *reinterpret_cast<uint2*>(q_out + row * K + (c + b) * kQK + sub * 8) =
-              make_uint2(lo, hi);
-          if (sub == 0) d_out[row * KB + c + b] = dbits;
-        }
-      }
-    };
-    if constexpr (X != 0) load_batch(0);   // row 0 < M: always live
-    // Weights: blocks past the wave's range re-read its last block (their
-    // terms are dropped below).
+  // The weights of a chunk: one 16-byte piece and one scale per lane, block
+  // and 32-row tile.  Blocks past the wave's range read as zero through the
+  // buffer range check (no memory access); their terms are dropped below.
+  auto load_weights = [&](int cc, v4i(&wv)[L][2], uint16_t(&wsc)[L][2]) {
 #pragma unroll
     for (int b = 0; b < L; ++b) {
-      const uint32_t kb = static_cast<uint32_t>(c + b < kb1 ? c + b : kb1 - 1);
+      const bool in = cc + b < kb1;
+      const uint32_t kb = static_cast<uint32_t>(cc + b);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        wv[b][j] = __builtin_amdgcn_raw_buffer_load_b128(rw, ow + j * 512 + kb * kGroupBlockBytes,
-                                                         0, 0);
-        wsc[b][j] = __builtin_amdgcn_raw_buffer_load_b16(rws, ows + j * 64 + kb * kGroupRows * 2,
-                                                         0, 0);
+        wv[b][j] = __builtin_amdgcn_raw_buffer_load_b128(
+            rw, in ? ow + j * 512 + kb * kGroupBlockBytes : kOutOfRange, 0, 0);
+        wsc[b][j] = __builtin_amdgcn_raw_buffer_load_b16(
+            rws, in ? ows + j * 64 + kb * kGroupRows * 2 : kOutOfRange, 0, 0);
       }
     }
-    if constexpr (X != 0) {
-      // into the slot (this wave's alone; a wave's LDS accesses complete in
-      // order, so no barrier).  Batches whose rows are all past M are
-      // skipped: those slot rows only feed outputs that are not stored.
-      constexpr int kRowsPerBatch = kPB * 64 / (4 * L);
-#pragma nounroll
-      for (int bt = 0; bt < kBatches && bt * kRowsPerBatch < M; ++bt) {
-        if (bt > 0) load_batch(bt);
-        quantize_batch(bt);
-      }
-    } else {
-      v4i xv[kSegs / 64];
-      uint16_t xs[kScs / 64];
-      // Activations: piece u*64 + lane is row s / (2L), 16 bytes s % (2L)
-      // of the chunk (16 consecutive lanes read 256 contiguous bytes of a
-      // row; rows past M, or bytes past the last block, read zero or are
-      // unused).
-#pragma unroll
-      for (int u = 0; u < kSegs / 64; ++u) {
-        const int sg = u * 64 + lane, row = sg / (2 * L), seg = sg % (2 * L);
-        xv[u] = __builtin_amdgcn_raw_buffer_load_b128(
-            ra, static_cast<uint32_t>(row * K + c * kQK + seg * 16), 0, 0);
-      }
-      // Activation scales: item u*64 + lane is row s / L, block s % L.
-#pragma unroll
-      for (int u = 0; u < kScs / 64; ++u) {
-        const int sc = u * 64 + lane, row = sc / L, b = sc % L;
-        xs[u] = __builtin_amdgcn_raw_buffer_load_b16(
-            rsa, c + b < kb1 ? static_cast<uint32_t>((row * KB + c + b) * 2) : kOutOfRange, 0,
-            0);
-      }
-      // into the slot (this wave's alone; no barrier)
-#pragma unroll
-      for (int u = 0; u < kSegs / 64; ++u) {
-        const int sg = u * 64 + lane, row = sg / (2 * L), seg = sg % (2 * L);
-        *reinterpret_cast<v4i*>(slot + row * kRow + seg * 16) = xv[u];
-      }
-#pragma unroll
-      for (int u = 0; u < kScs / 64; ++u) {
-        const int sc = u * 64 + lane, row = sc / L, b = sc % L;
-        sslot[((row >> 5) * L + b) * 32 + rot4(row & 31)] = f16_bits_to_f32(xs[u]);
-      }
-    }
+  };
+  // A chunk's block dots and epilogue, from its weights and the slot.
+  auto compute = [&](int c, const v4i(&wv)[L][2], const uint16_t(&wsc)[L][2]) {
 #pragma unroll
     for (int b = 0; b < L; ++b) {
       const float live = c + b < kb1 ? 1.0f : 0.0f;
@@ -1063,6 +968,135 @@ __global__ __launch_bounds__(W * 64) void gemm_q8_small_kernel(
           }
         }
       }
+      // one block at a time: hoisting later blocks' MFMAs needs a result
+      // tile of registers each
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if constexpr (X == 0) {
+    // Software pipeline: each chunk issues its activation loads, then the
+    // next chunk's weight loads, then waits for the activations only (loads
+    // complete in order), so the weight stream stays in flight through the
+    // chunk's arithmetic.
+    v4i wv[L][2];
+    uint16_t wsc[L][2];
+    load_weights(kb0, wv, wsc);
+#pragma nounroll
+    for (int c = kb0; c < kb1; c += L) {
+      v4i xv[kSegs / 64];
+      uint16_t xs[kScs / 64];
+      // Activations: piece u*64 + lane is row s / (2L), 16 bytes s % (2L)
+      // of the chunk (16 consecutive lanes read 256 contiguous bytes of a
+      // row; rows past M, or bytes past the last block, read zero or are
+      // unused).
+#pragma unroll
+      for (int u = 0; u < kSegs / 64; ++u) {
+        const int sg = u * 64 + lane, row = sg / (2 * L), seg = sg % (2 * L);
+        xv[u] = __builtin_amdgcn_raw_buffer_load_b128(
+            ra, static_cast<uint32_t>(row * K + c * kQK + seg * 16), 0, 0);
+      }
+      // Activation scales: item u*64 + lane is row s / L, block s % L.
+#pragma unroll
+      for (int u = 0; u < kScs / 64; ++u) {
+        const int sc = u * 64 + lane, row = sc / L, b = sc % L;
+        xs[u] = __builtin_amdgcn_raw_buffer_load_b16(
+            rsa, c + b < kb1 ? static_cast<uint32_t>((row * KB + c + b) * 2) : kOutOfRange, 0,
+            0);
+      }
+      v4i wn[L][2];
+      uint16_t wsn[L][2];
+      load_weights(c + L, wn, wsn);
+      // into the slot (this wave's alone; no barrier)
+#pragma unroll
+      for (int u = 0; u < kSegs / 64; ++u) {
+        const int sg = u * 64 + lane, row = sg / (2 * L), seg = sg % (2 * L);
+        *reinterpret_cast<v4i*>(slot + row * kRow + seg * 16) = xv[u];
+      }
+#pragma unroll
+      for (int u = 0; u < kScs / 64; ++u) {
+        const int sc = u * 64 + lane, row = sc / L, b = sc % L;
+        sslot[((row >> 5) * L + b) * 32 + rot4(row & 31)] = f16_bits_to_f32(xs[u]);
+      }
+      compute(c, wv, wsc);
+#pragma unroll
+      for (int b = 0; b < L; ++b)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          wv[b][j] = wn[b][j];
+          wsc[b][j] = wsn[b][j];
+        }
+    }
+  } else {
+    for (int c = kb0; c < kb1; c += L) {
+      v4i wv[L][2];
+      uint16_t wsc[L][2];
+      // Raw activations (X != 0): item t = u*64 + lane is row t / (4L), block
+      // (t / 4) % L, values 8*(t % 4) .. +8 of it, so four lanes hold a block
+      // and 4L consecutive lanes a contiguous run of a row.  The first batch of
+      // items is loaded before the weights, the rest after.
+      constexpr int kItems = MT * 32 * L * 4;
+      constexpr int kPB = X == 1 ? 4 : 8;   // items per lane per batch: 32 registers
+      constexpr int kBatches = X == 0 ? 1 : kItems / 64 / kPB;
+      static_assert(X == 0 || kItems % (64 * kPB) == 0, "whole batches");
+      v4i raw[kPB][kEsz / 2];
+      auto load_batch = [&](int bt) {
+#pragma unroll
+        for (int e = 0; e < kPB; ++e) {
+          const int t = (bt * kPB + e) * 64 + lane;
+          const int row = t / (4 * L), b = (t / 4) % L, sub = t % 4;
+          const uint32_t off =
+              c + b < kb1 ? static_cast<uint32_t>((row * ldx + (c + b) * kQK + sub * 8) * kEsz)
+                          : kOutOfRange;
+#pragma unroll
+          for (int h = 0; h < kEsz / 2; ++h)
+            raw[e][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                ra, off == kOutOfRange ? kOutOfRange : off + 16 * h, 0, 0);
+        }
+      };
+      auto quantize_batch = [&](int bt) {
+#pragma unroll
+        for (int e = 0; e < kPB; ++e) {
+          const int t = (bt * kPB + e) * 64 + lane;
+          const int row = t / (4 * L), b = (t / 4) % L, sub = t % 4;
+          float v[8];
+          if constexpr (X == 1) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[4 * h + q] = __int_as_float(raw[e][h][q]);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t w = static_cast<uint32_t>(raw[e][0][q]);
+              v[2 * q] = __uint_as_float(w << 16);
+              v[2 * q + 1] = __uint_as_float(w & 0xffff0000u);
+            }
+          }
+          uint32_t lo, hi;
+          uint16_t dbits;
+          quantize8(v, lo, hi, dbits);   // all lanes take part (lane exchanges)
+          *reinterpret_cast<uint2*>(slot + row * kRow + b * kQK + sub * 8) = make_uint2(lo, hi);
+          if (sub == 0) sslot[((row >> 5) * L + b) * 32 + rot4(row & 31)] = f16_bits_to_f32(dbits);
+          if (store_q && row < M && c + b < kb1) {
+            *reinterpret_cast<uint2*>(q_out + row * K + (c + b) * kQK + sub * 8) =
+                make_uint2(lo, hi);
+            if (sub == 0) d_out[row * KB + c + b] = dbits;
+          }
+        }
+      };
+      load_batch(0);   // row 0 < M: always live
+      load_weights(c, wv, wsc);
+      // into the slot (this wave's alone; a wave's LDS accesses complete in
+      // order, so no barrier).  Batches whose rows are all past M are
+      // skipped: those slot rows only feed outputs that are not stored.
+      constexpr int kRowsPerBatch = kPB * 64 / (4 * L);
+#pragma nounroll
+      for (int bt = 0; bt < kBatches && bt * kRowsPerBatch < M; ++bt) {
+        if (bt > 0) load_batch(bt);
+        quantize_batch(bt);
+      }
+      compute(c, wv, wsc);
     }
   }
 
