@@ -263,7 +263,8 @@ q8_status q8_pack_weights_gateup(const void *w_gate, const void *w_up, int64_t I
  *
  * q_a, d_a  the quantised activations [M][K] (as for q8_gemm).
  * w_packed  the output of q8_pack_weights_gateup for the same I and K.
- * q_h   [M][I] int8 out; d_h [M][I/32] binary16 out (2-byte aligned).
+ * q_h   [M][I] int8 out (16-byte aligned); d_h [M][I/32] binary16 out
+ *       (2-byte aligned).
  *
  * Errors: Q8_ERR_NULL, Q8_ERR_SHAPE (I < 32 or I % 32 != 0, bad K or M),
  * Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH.

@@ -213,7 +213,8 @@ q8_status q8_gemm_swiglu(int64_t M, int64_t I, int64_t K, const int8_t* q_a, con
   if (q_a == nullptr || d_a == nullptr || w_packed == nullptr || q_h == nullptr ||
       d_h == nullptr)
     return Q8_ERR_NULL;
-  if (!aligned(q_a, 16) || !aligned(d_a, 2) || !aligned(w_packed, 16) || !aligned(d_h, 2))
+  if (!aligned(q_a, 16) || !aligned(d_a, 2) || !aligned(w_packed, 16) || !aligned(q_h, 16) ||
+      !aligned(d_h, 2))
     return Q8_ERR_ALIGN;
   if (((M + 127) / 128) * ((2 * I + 127) / 128) >= kMaxDim) return Q8_ERR_SHAPE;
   const q8_status dev = check_device();

@@ -760,28 +760,67 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   if constexpr (kSwiglu) {
     // Each 64 columns of the wave are one row group: column 64p + l32 is the
     // gate of hidden unit 32*grp + l32 and column 64p + 32 + l32 its up, both
-    // in this lane (j = 2p and 2p + 1); a half-wave's 32 lanes hold one
-    // 32-unit block of a row.
+    // in this lane (j = 2p and 2p + 1).  The lane forms h = silu(g) * u for
+    // its 16 rows of each group, and the wave passes the values through LDS
+    // (the stage buffers, free now) so that one lane holds a whole Q8_0
+    // block of h (32 hidden units of one row): it takes the block's maximum
+    // and scale itself and writes its 32 codes with two 16-byte stores.
     static_assert(T::MF == 32 && T::TN % 2 == 0, "whole 64-column row groups per wave");
-    const int64_t I = N / 2;
+    constexpr int kGroups = TN / 2;
+    constexpr int kBlocks = TM * 32 * kGroups;   // (row, group) blocks of the wave tile
+    constexpr int kPitch = 36;                   // floats per block in LDS (32 + 4: banks)
+    static_assert(T::kWavesT * kBlocks * kPitch * 4 <= T::NBUF * T::kStage, "LDS");
+    float* const hb = reinterpret_cast<float*>(smem) + wt * kBlocks * kPitch;
+    __syncthreads();   // every wave is done with the stage buffers, and its loads into them
 #pragma unroll
-    for (int pr = 0; pr < TN / 2; ++pr) {
-      const int64_t grp = (n0 + wn0) / kGroupRows + pr;
-      if (grp * kGroupRows >= N) continue;
-      const int64_t hid = grp * 32 + l32;
+    for (int pr = 0; pr < kGroups; ++pr)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-          uint16_t dbits;
-          const int q =
-              quantize_lane32(silu_mul(acc[i][2 * pr][r], acc[i][2 * pr + 1][r]), dbits);
-          if (row < M) {
-            q_h[row * I + hid] = static_cast<int8_t>(q);
-            if (l32 == 0) d_h[row * (I / kQK) + grp] = dbits;
-          }
+          const int rt = 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);   // row in the wave tile
+          hb[(rt * kGroups + pr) * kPitch + l32] =
+              silu_mul(acc[i][2 * pr][r], acc[i][2 * pr + 1][r]);
         }
+    // the wave's own values, written by other lanes: its LDS accesses
+    // complete in order, so a wave-level fence suffices
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t I = N / 2;
+    for (int bk = lane_o; bk < kBlocks; bk += 64) {
+      const int rt = bk / kGroups, pr = bk % kGroups;
+      const int64_t row = m0 + wm0 + rt;
+      const int64_t grp = (n0 + wn0) / kGroupRows + pr;
+      if (row >= M || grp * kGroupRows >= N) continue;
+      float h[32];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const v4f v = *reinterpret_cast<const v4f*>(hb + bk * kPitch + 4 * c);
+        h[4 * c] = v.x;
+        h[4 * c + 1] = v.y;
+        h[4 * c + 2] = v.z;
+        h[4 * c + 3] = v.w;
+      }
+      float amax = fabsf(h[0]);
+#pragma unroll
+      for (int e = 1; e < 32; ++e) amax = fmaxf(amax, fabsf(h[e]));
+      float id;
+      uint16_t dbits;
+      const bool nz = block_scale(amax, id, dbits);
+      uint32_t w[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        w[c] = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[c] |= (nz ? static_cast<uint32_t>(block_code(h[4 * c + e], id)) & 0xffu : 0u)
+                  << (8 * e);
+      }
+      uint4* const qo = reinterpret_cast<uint4*>(q_h + row * I + grp * kQK);
+      qo[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      qo[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      d_h[row * (I / kQK) + grp] = dbits;
     }
     return;
   }

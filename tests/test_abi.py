@@ -146,6 +146,7 @@ def test_gemm_swiglu_validation(L):
     assert f(4, 64, 64, ODD, FAKE, FAKE, FAKE, FAKE, None) == ALIGN
     assert f(4, 64, 64, FAKE, ODD, FAKE, FAKE, FAKE, None) == ALIGN
     assert f(4, 64, 64, FAKE, FAKE, ODD, FAKE, FAKE, None) == ALIGN
+    assert f(4, 64, 64, FAKE, FAKE, FAKE, ODD, FAKE, None) == ALIGN
     assert f(4, 64, 64, FAKE, FAKE, FAKE, FAKE, ODD, None) == ALIGN
 
 
