@@ -88,6 +88,7 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 constexpr float kBias = 12582912.0f;            // 1.5 * 2^23
 constexpr int kBiasBits = 0x4B400000;           // its binary32 bits
 [[maybe_unused]] constexpr uint32_t kOutOfRange = 0xFFFFFFFFu;   // buffer offset that reads as zero
+constexpr int kStoreNT = 2;   // cache-policy operand of a buffer store: non-temporal
 
 // MF: output tile of one MFMA, 32 (v_mfma_i32_32x32x32_i8) or 16
 // (v_mfma_i32_16x16x32_i8).
@@ -830,6 +831,8 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
   // tile's offsets fit 31 bits: rows past M fall outside the range, and a
   // lane whose column is past N takes an offset of 2^31 and above, also
   // outside it, so the stores need no branches and one 32-bit add each.
+  // The stores are marked non-temporal (C is not read again here), which
+  // leaves more of the caches to the operand panels.
   if (int64_t(BM) * ldc * 4 <= (int64_t(1) << 31)) {
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(C + m0 * ldc, static_cast<uint32_t>(rows_valid * ldc * 4));
@@ -847,7 +850,7 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
           const uint32_t roff =
               static_cast<uint32_t>(T::MF * i + (T::MF == 32 ? 8 * (r >> 2) + (r & 3) : r)) * ldc4;
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, lane_off + roff,
-                                                0, 0);
+                                                0, kStoreNT);
         }
     }
     return;
@@ -888,7 +891,9 @@ void gemm_q8_mfma_kernel(const int8_t* __restrict__ q_a, const uint16_t* __restr
 //     own and reads back with broadcast loads for its accumulator rows.
 // One v_mfma_i32_32x32x32_i8 per 32x32 tile and block, the bias-fold
 // epilogue of the tiled kernel, and the 8 waves' partial sums added in a
-// fixed pairwise tree through LDS.
+// fixed pairwise tree through LDS.  With quantised activations a wave
+// issues the next chunk's weight loads before the current chunk's block
+// dots (a second set of weight registers), so the stream stays in flight.
 //
 // X selects the activation input: 0, quantised rows q_a/d_a; 1 (binary32)
 // or 2 (bfloat16), unquantised rows x that every wave quantises for its own
