@@ -65,15 +65,19 @@ inline bool order_admissible(int order, int64_t tiles_m, int64_t tiles_n) {
 }
 
 // The order the launcher picks: contiguous per XCD when the grid splits
-// evenly over the 8 XCDs, and rectangles when one XCD's share of activation
-// rows (tiles_m * BM rows of K bytes) would not fit its 4 MB L2.
+// evenly over the 8 XCDs and the activation rows of a tile column (tiles_m
+// * BM rows of K bytes) fit an XCD's 4 MB L2; rectangles when the rows of
+// one rectangle do; otherwise plain.  In that last case the contiguous
+// order would give each XCD a strip of one tile column, whose concurrent
+// tiles all read different activation rows, while the plain order spreads
+// an XCD's concurrent tiles over a few rows and columns of tiles.
 inline int choose_order(int64_t tiles_m, int64_t tiles_n, int64_t bm, int64_t K) {
   if ((tiles_m * tiles_n) % 8 != 0) return 0;
   constexpr int64_t kL2Bytes = int64_t(4) << 20;
-  if (tiles_m * bm * K > kL2Bytes)
-    for (int sm = 2; sm <= 8; sm *= 2)
-      if (order_admissible(sm, tiles_m, tiles_n) && tiles_m / sm * bm * K <= kL2Bytes) return sm;
-  return 1;
+  if (tiles_m * bm * K <= kL2Bytes) return 1;
+  for (int sm = 2; sm <= 8; sm *= 2)
+    if (order_admissible(sm, tiles_m, tiles_n) && tiles_m / sm * bm * K <= kL2Bytes) return sm;
+  return 0;
 }
 
 // A BM x BN tile addresses its BM rows of q_a (BM*K bytes) and its BN/64

@@ -92,6 +92,11 @@ int main() {
   if (q8::order_admissible(1, 3, 5)) fail("order 1 on 15 tiles admitted", 3, 5, 1);
   // the prefill grid takes the 2 x 4 rectangles
   if (q8::choose_order(16, 96, 128, 4096) != 2) fail("prefill grid order", 16, 96, 2);
+  // a grid whose rows fit no rectangle's L2 share takes the plain order
+  // (large down: 64 x 40 tiles of 128 rows at K = 17408), and a grid whose
+  // rows all fit takes the contiguous one (M512 on 128-row tiles)
+  if (q8::choose_order(64, 40, 128, 17408) != 0) fail("large grid order", 64, 40, 0);
+  if (q8::choose_order(4, 64, 128, 4096) != 1) fail("small grid order", 4, 64, 1);
   // 32-bit buffer ranges: a 128x256 tile cannot hold K = 2^24, a 128x128 can
   if (q8::buffer_ranges_fit(128, 256, 1LL << 24)) fail("128x256 at K=2^24 fits", 128, 256, 0);
   if (!q8::buffer_ranges_fit(128, 128, 1LL << 24)) fail("128x128 at K=2^24 does not fit", 128, 128, 0);
