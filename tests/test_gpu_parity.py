@@ -85,13 +85,16 @@ def test_quantize_guard_bands(orc, dtype, M, K):
     assert np.array_equal(qh[1:M + 1], qr) and np.array_equal(dh[1:M + 1], dr)
 
 
-def test_quantize_rows_past_grid_limit(orc):
+@pytest.mark.parametrize("M,K", [(4 * 65535 + 4 * 37 + 3, 64), (65536 + 300, 2048)])
+def test_quantize_rows_past_grid_limit(orc, M, K):
     """More rows than a launch grid holds in y (65535): the workgroups loop
-    over further rows and stop at M."""
-    M, K = 4 * 65535 + 4 * 37 + 3, 64
+    over further rows and stop at M (four lanes per block at K = 64, one lane
+    per block at K = 2048)."""
     r = np.random.default_rng(41)
-    x = (r.standard_normal((M, K)) * 2.0 ** r.uniform(-8, 8, (M, 1))).astype(np.float32)
+    x = r.standard_normal((M, K), dtype=np.float32)
+    x *= (2.0 ** r.uniform(-8, 8, (M, 1))).astype(np.float32)
     xs = workloads.f32_to_bf16_bits(x)
+    del x
     say("quantize bf16 M=%d K=%d (rows past the grid's y limit)" % (M, K))
     qbuf = torch.full((M + 1, K), 77, dtype=torch.int8, device=DEV)
     dbuf = torch.full((M + 1, K // 32), 3.0, dtype=torch.float16, device=DEV)
